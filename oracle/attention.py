@@ -1,0 +1,270 @@
+"""Exact softmax attention in fp64 on the CPU, written out the plain way.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): the product path never
+imports this module.
+
+What it computes, with where each step is defined:
+
+* ``S = Q·Kᵀ/√d``, ``P = softmax(S)`` row by row, ``O = P·V`` -- the three-line
+  definition at the top of "Attention from the kernel's side: FlashAttention,
+  online softmax and fused dequant", and the three steps of the "Concept"
+  section of "Attention kernels".  The scale is passed in explicitly so the
+  harness can hand the oracle exactly the value the GPU receives.
+* Each softmax row subtracts its maximum before exponentiating ("The online
+  softmax" section of the first page).  In fp64 this only matters for range,
+  but it is the stated definition.
+* Causal: key ``j`` is visible to query ``i`` iff ``j <= i`` ("Masking
+  variants", section 5 of "Attention Computation in Practice"); the problem is
+  square (as many queries as keys).
+* Grouped-query attention: query head ``h`` reads KV head ``h // (Hq // Hkv)``
+  ("GQA in the kernel", same section).
+* Decode: one query per sequence sees keys ``0 .. kv_len-1`` of its cache and
+  nothing past them ("Prefill and decode are different problems" on the first
+  page; "Concept" on "Attention kernels").
+* A partial state ``(m, l, o)`` over a set of keys is the running maximum, the
+  sum of ``exp(s_j - m)`` and the unnormalised ``sum_j exp(s_j - m) v_j``;
+  two states merge by ``m = max(m_a, m_b)``, ``l = l_a e^(m_a-m) + l_b e^(m_b-m)``,
+  ``o = o_a e^(m_a-m) + o_b e^(m_b-m)`` ("Maths" section of "Attention
+  kernels"), where a state with ``m = -inf`` (no keys) contributes a factor 0
+  (the guard in that page's "Code" section).  The output is ``o / l``.
+
+Readings where the pages are silent (each is listed in the design doc):
+
+* A row with no visible key (decode with ``kv_len = 0``, an all-empty merge)
+  returns 0.  The pages leave softmax over no keys undefined.
+* Causal attention is only defined for square problems here.
+
+``online_softmax_tiled`` and ``split_partials`` are second implementations used
+only by the oracle's own self-tests: the recurrence of "The online softmax" and
+of "03 · The structure" on "Quantized kernels", and the split-K slices of
+"Attention kernels".
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+NEG_INF = float("-inf")
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def kv_head_of(h: int, hq: int, hkv: int) -> int:
+    """KV head read by query head ``h``: plain index arithmetic, no copy
+    ("GQA in the kernel", "Attention Computation in Practice" section 5)."""
+    if hkv < 1 or hq % hkv:
+        raise ValueError(f"hq={hq} is not a multiple of hkv={hkv}")
+    return h // (hq // hkv)
+
+
+def _materialised_rows(q_rows, K, V, scale, row_index=None):
+    """Softmax attention of a block of query rows over keys ``K`` / values ``V``.
+
+    The whole block of score rows is materialised (as the textbook version on
+    "Attention Computation in Practice", section 4, does one row at a time),
+    masked, shifted by its row maximum, exponentiated, normalised by its row sum
+    and multiplied by V.  ``row_index`` gives each row's query position when the
+    causal mask applies, else ``None``.
+    """
+    S = scale * (q_rows @ K.T)
+    if row_index is not None:
+        j = np.arange(K.shape[0])
+        S = np.where(j[None, :] <= np.asarray(row_index)[:, None], S, -np.inf)
+    if S.shape[1] == 0:
+        return np.zeros((q_rows.shape[0], V.shape[1]))
+    m = S.max(axis=1, keepdims=True)
+    has_key = np.isfinite(m)
+    E = np.exp(S - np.where(has_key, m, 0.0))  # masked scores give exp(-inf) = 0
+    Z = E.sum(axis=1, keepdims=True)
+    O = (E @ V) / np.where(has_key, Z, 1.0)
+    return np.where(has_key, O, 0.0)
+
+
+def attention(q, k, v, scale: float, causal: bool = False, row_block: int = 256):
+    """Exact attention for ``q: [B, Hq, N, d]`` and ``k, v: [B, Hkv, Nk, d]``.
+
+    Returns ``O: [B, Hq, N, d]`` in fp64.  Works per (batch, query head) over
+    blocks of ``row_block`` query rows.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Hq, N, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if (Bk, dk) != (B, d) or v.shape != k.shape:
+        raise ValueError("q, k, v shapes disagree")
+    if causal and Nk != N:
+        raise ValueError("causal attention is defined here for square problems only")
+    out = np.zeros((B, Hq, N, d))
+    for b in range(B):
+        for h in range(Hq):
+            kh = kv_head_of(h, Hq, Hkv)
+            for i0 in range(0, N, row_block):
+                i1 = min(N, i0 + row_block)
+                rows = np.arange(i0, i1) if causal else None
+                out[b, h, i0:i1] = _materialised_rows(q[b, h, i0:i1], k[b, kh], v[b, kh], scale, rows)
+    return out
+
+
+def attention_rows(q_rows, K, V, scale: float, row_index=None):
+    """Exact attention of selected query rows of one head.
+
+    ``q_rows: [R, d]``, ``K, V: [Nk, d]``; ``row_index`` (length R) gives each
+    row's position for the causal mask, or ``None`` for no mask.  Used to check
+    sampled rows of outputs too large to recompute whole.
+    """
+    return _materialised_rows(_f64(q_rows), _f64(K), _f64(V), scale, row_index)
+
+
+def softmax_probabilities(q, k, scale: float, causal: bool = False):
+    """The materialised probability matrix ``P = softmax(scale·Q·Kᵀ)`` of one
+    head (``q: [N, d]``, ``k: [Nk, d]``), for checks on P itself."""
+    q, k = _f64(q), _f64(k)
+    S = scale * (q @ k.T)
+    if causal:
+        i = np.arange(q.shape[0])[:, None]
+        j = np.arange(k.shape[0])[None, :]
+        S = np.where(j <= i, S, -np.inf)
+    m = S.max(axis=1, keepdims=True)
+    E = np.exp(S - m)
+    return E / E.sum(axis=1, keepdims=True)
+
+
+def decode(q, k_cache, v_cache, kv_lens, scale: float):
+    """Single-query attention over a KV cache.
+
+    ``q: [B, Hq, d]``, ``k_cache, v_cache: [B, Hkv, Lmax, d]``, ``kv_lens: [B]``.
+    Query ``(b, h)`` sees cache rows ``0 .. kv_lens[b]-1`` of KV head
+    ``h // (Hq // Hkv)``; rows at or past ``kv_lens[b]`` are never read.
+    Returns ``O: [B, Hq, d]`` in fp64.
+    """
+    q = _f64(q)
+    B, Hq, d = q.shape
+    Hkv = k_cache.shape[1]
+    g = Hq // Hkv
+    kv_head_of(0, Hq, Hkv)
+    out = np.zeros((B, Hq, d))
+    for b in range(B):
+        L = int(kv_lens[b])
+        if not 0 <= L <= k_cache.shape[2]:
+            raise ValueError(f"kv_lens[{b}]={L} outside [0, {k_cache.shape[2]}]")
+        for kh in range(Hkv):
+            K = _f64(k_cache[b, kh, :L])
+            V = _f64(v_cache[b, kh, :L])
+            out[b, kh * g:(kh + 1) * g] = _materialised_rows(q[b, kh * g:(kh + 1) * g], K, V, scale)
+    return out
+
+
+def _merge_arrays(ma, la, oa, mb, lb, ob):
+    """The two-state merge rule, elementwise over any leading shape.
+
+    ``m = max(m_a, m_b)``; each side is weighted by ``exp(m_side - m)``, or by 0
+    when that side holds no keys (``m_side = -inf``), which also keeps
+    ``-inf - (-inf)`` from ever being evaluated.
+    """
+    m = np.maximum(ma, mb)
+    m_safe = np.where(m == -np.inf, 0.0, m)
+    fa = np.where(ma == -np.inf, 0.0, np.exp(np.where(ma == -np.inf, m_safe, ma) - m_safe))
+    fb = np.where(mb == -np.inf, 0.0, np.exp(np.where(mb == -np.inf, m_safe, mb) - m_safe))
+    l = la * fa + lb * fb
+    o = oa * np.asarray(fa)[..., None] + ob * np.asarray(fb)[..., None]
+    return m, l, o
+
+
+def empty_partial(d: int):
+    """The state of a worker that saw no keys: ``(-inf, 0, 0)``."""
+    return (NEG_INF, 0.0, np.zeros(d))
+
+
+
+def merge_pair(a, b):
+    """Merge two partial states ``(m, l, o)`` into one."""
+    m, l, o = _merge_arrays(_f64(a[0]), _f64(a[1]), _f64(a[2]), _f64(b[0]), _f64(b[1]), _f64(b[2]))
+    return (float(m), float(l), o)
+
+
+def merge_partials(m, l, o):
+    """Fold partial states along their last state axis and normalise.
+
+    ``m, l: [..., S]``, ``o: [..., S, d]`` (natural-log units: ``m`` is a
+    maximum of scaled scores, ``l`` and ``o`` are taken relative to ``e^m``).
+    Returns ``O = o / l`` with shape ``[..., d]``, and 0 where no partial held a
+    key.
+    """
+    m, l, o = _f64(m), _f64(l), _f64(o)
+    S = m.shape[-1]
+    acc_m = np.full(m.shape[:-1], -np.inf)
+    acc_l = np.zeros(m.shape[:-1])
+    acc_o = np.zeros(o.shape[:-2] + (o.shape[-1],))
+    for s in range(S):
+        acc_m, acc_l, acc_o = _merge_arrays(acc_m, acc_l, acc_o, m[..., s], l[..., s], o[..., s, :])
+    has_key = (acc_l > 0)[..., None]
+    return np.where(has_key, acc_o / np.where(has_key, acc_l[..., None], 1.0), 0.0)
+
+
+def split_partials(q_row, K, V, scale: float, workers: int):
+    """Split-K: ``workers`` contiguous key slices, one partial state each.
+
+    Worker ``w`` takes keys ``[w·n // W, (w+1)·n // W)``; with more workers than
+    keys some slices are empty and give ``(-inf, 0, 0)``.  Each partial is the
+    plain definition over its slice: ``m`` the slice's largest scaled score,
+    ``l = sum exp(s_j - m)``, ``o = sum exp(s_j - m) v_j``.
+    """
+    q_row, K, V = _f64(q_row), _f64(K), _f64(V)
+    n = K.shape[0]
+    parts = []
+    for w in range(workers):
+        j0, j1 = (w * n) // workers, ((w + 1) * n) // workers
+        if j1 <= j0:
+            parts.append(empty_partial(V.shape[1]))
+            continue
+        s = scale * (K[j0:j1] @ q_row)
+        m = float(s.max())
+        e = np.exp(s - m)
+        parts.append((m, float(e.sum()), e @ V[j0:j1]))
+    return parts
+
+
+def online_softmax_tiled(q, k, v, scale: float, causal: bool = False, tile: int = 128):
+    """The online-softmax recurrence over key tiles of ``tile`` keys, one head.
+
+    ``q: [N, d]``, ``k, v: [Nk, d]``.  Per query row the state starts at
+    ``m = -inf, l = 0, o = 0``; for each tile ``m_new = max(m, max_j s_j)``,
+    ``alpha = exp(m - m_new)`` (0 while ``m = -inf``),
+    ``l = alpha·l + sum_j exp(s_j - m_new)``,
+    ``o = alpha·o + sum_j exp(s_j - m_new)·v_j``, ``m = m_new``; finally
+    ``O = o / l``.  All rows advance together; under the causal mask a row's
+    keys past its own position score ``-inf`` and so change nothing.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    N, d = q.shape
+    Nk = k.shape[0]
+    if tile < 1:
+        raise ValueError("tile must be >= 1")
+    m = np.full(N, -np.inf)
+    l = np.zeros(N)
+    o = np.zeros((N, v.shape[1]))
+    rows = np.arange(N)[:, None]
+    for j0 in range(0, Nk, tile):
+        j1 = min(Nk, j0 + tile)
+        s = scale * (q @ k[j0:j1].T)
+        if causal:
+            s = np.where(np.arange(j0, j1)[None, :] <= rows, s, -np.inf)
+        m_new = np.maximum(m, s.max(axis=1))
+        live = m_new != -np.inf
+        m_new_safe = np.where(live, m_new, 0.0)
+        alpha = np.where(m == -np.inf, 0.0, np.exp(np.where(m == -np.inf, m_new_safe, m) - m_new_safe))
+        p = np.where(live[:, None], np.exp(s - m_new_safe[:, None]), 0.0)
+        l = alpha * l + p.sum(axis=1)
+        o = alpha[:, None] * o + p @ v[j0:j1]
+        m = m_new
+    has_key = (l > 0)[:, None]
+    return np.where(has_key, o / np.where(has_key, l[:, None], 1.0), 0.0)
+
+
+def fp16_exp_overflow_threshold() -> float:
+    """Largest x with exp(x) finite in IEEE binary16: ln(65504) ≈ 11.09
+    ("The online softmax" on the first page)."""
+    return math.log(65504.0)

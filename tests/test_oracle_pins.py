@@ -1,0 +1,340 @@
+"""Pins of the fp64 oracle to things other than itself (CPU only).
+
+Each test checks the oracle against a closed form, an invariant, a special case
+that reduces to a textbook or library routine, or a figure the pages print.
+They are chosen so that a plausible slip in the oracle -- a dropped term, a
+wrong sign or index, a transposed operand, an off-by-one in the causal mask or
+in a cache length, a wrong GQA mapping, a missing guard -- fails at least one.
+"""
+
+import json
+import math
+import pathlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+GOLDEN = json.loads((pathlib.Path(__file__).parent / "golden" / "pages_worked_figures.json").read_text())
+TOL = GOLDEN["test_contract"]["tolerance"]  # 1e-12, "Attention kernels", 'Code'
+
+
+def gauss(seed, *shape):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def one_head(q, k, v, scale, causal):
+    return oracle.attention(q[None, None], k[None, None], v[None, None], scale, causal)[0, 0]
+
+
+# --- tiled recurrence vs the materialised definition ------------------------------------
+
+@pytest.mark.parametrize("tile", [1, 2, 3, 7, 8, 64, 128, 256, 511, 512])
+def test_tiled_equals_naive_at_go_example_shape(tile):
+    g = GOLDEN["go_example"]
+    n, d = g["seq"], g["head_dim"]
+    q, k, v = gauss(1, n, d), gauss(2, n, d), gauss(3, n, d)
+    scale = 1 / math.sqrt(d)
+    ref = one_head(q, k, v, scale, causal=True)
+    got = oracle.online_softmax_tiled(q, k, v, scale, causal=True, tile=tile)
+    assert np.max(np.abs(got - ref)) <= TOL
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("tile", [1, 8, 47, 48])
+def test_tiled_equals_naive_at_widget_shape(causal, tile):
+    g = GOLDEN["widget_tiling"]
+    nq, nk, d = g["queries"], g["keys"], g["head_dim"]
+    q, k, v = gauss(4, nq, d), gauss(5, nk, d), gauss(6, nk, d)
+    ref = one_head(q, k, v, 0.25, causal)
+    got = oracle.online_softmax_tiled(q, k, v, 0.25, causal=causal, tile=tile)
+    assert np.max(np.abs(got - ref)) <= TOL
+
+
+def test_tiled_differs_from_unrescaled_variant():
+    """The rescale by exp(m - m_new) matters: dropping it (keeping l and o as they
+    were) gives a visibly different answer on the same data, so the agreement
+    above is not vacuous."""
+    n, d = 64, 16
+    q, k, v = gauss(7, n, d), gauss(8, n, d), gauss(9, n, d)
+    k[40] *= 6.0  # a late, large score forces a rescale
+    scale = 0.5
+    ref = one_head(q, k, v, scale, causal=False)
+    # same recurrence with alpha forced to 1 and p taken against the *tile* max
+    m = np.full(n, -np.inf); l = np.zeros(n); o = np.zeros((n, d))
+    for j0 in range(0, n, 8):
+        s = scale * q @ k[j0:j0 + 8].T
+        m_new = np.maximum(m, s.max(1))
+        p = np.exp(s - m_new[:, None])
+        l = l + p.sum(1); o = o + p @ v[j0:j0 + 8]; m = m_new
+    assert np.max(np.abs(o / l[:, None] - ref)) > 1e-3
+
+
+# --- split-K and the merge rule --------------------------------------------------------
+
+def fold_left(parts):
+    acc = oracle.empty_partial(parts[0][2].shape[0])
+    for p in parts:
+        acc = oracle.merge_pair(acc, p)
+    return acc
+
+
+def finish(state):
+    m, l, o = state
+    return o / l
+
+
+@pytest.mark.parametrize("workers", [1, 2, 3, 4, 7, 1000, 1500])
+def test_splitk_equals_naive_1000_keys(workers):
+    c = GOLDEN["test_contract"]
+    n, d = c["split_keys"], 16
+    q, k, v = gauss(10, d), gauss(11, n, d) * 2.0, gauss(12, n, d)
+    ref = one_head(q[None], k, v, 0.25, causal=False)[0]
+    parts = oracle.split_partials(q, k, v, 0.25, workers)
+    assert len(parts) == workers
+    if workers > n:
+        assert sum(1 for p in parts if p[0] == -np.inf) == workers - n
+    assert np.max(np.abs(finish(fold_left(parts)) - ref)) <= TOL
+    # the array form used to check GPU partials gives the same answer
+    m = np.array([p[0] for p in parts]); l = np.array([p[1] for p in parts])
+    o = np.stack([p[2] for p in parts])
+    assert np.max(np.abs(oracle.merge_partials(m, l, o) - ref)) <= TOL
+
+
+def test_splitk_widget_4096_keys_4_workers():
+    g = GOLDEN["widget_splitk"]
+    d = 16
+    q = gauss(13, d) * 3.0
+    k, v = gauss(14, g["keys"], d), gauss(15, g["keys"], d)
+    ref = one_head(q[None], k, v, 1 / math.sqrt(d), causal=False)[0]
+    parts = oracle.split_partials(q, k, v, 1 / math.sqrt(d), g["workers"])
+    assert np.max(np.abs(finish(fold_left(parts)) - ref)) <= TOL
+    # the invariants the printed partials satisfy (their inputs are not given):
+    # each slice's l lies in [1, slice length] and the merged max is the largest m_s
+    slice_len = g["keys"] // g["workers"]
+    for m_s, l_s, _ in parts:
+        assert 1.0 <= l_s <= slice_len
+    assert fold_left(parts)[0] == max(p[0] for p in parts)
+    for m_s, l_s in g["printed_partials_m_l"]:
+        assert 1.0 <= l_s <= slice_len
+    printed_m = [m for m, _ in g["printed_partials_m_l"]]
+    assert max(printed_m) == printed_m[0] == 16.81
+
+
+@pytest.mark.parametrize("order", ["left", "right", "tree", "shuffled"])
+def test_merge_order_does_not_matter(order):
+    """'correct for any block order' (Quantized kernels, '02 · The insight')."""
+    n, d = 777, 8
+    q, k, v = gauss(16, d), gauss(17, n, d) * 3.0, gauss(18, n, d)
+    ref = one_head(q[None], k, v, 0.3, causal=False)[0]
+    parts = oracle.split_partials(q, k, v, 0.3, 13)
+    if order == "left":
+        st = fold_left(parts)
+    elif order == "right":
+        st = parts[-1]
+        for p in reversed(parts[:-1]):
+            st = oracle.merge_pair(p, st)
+    elif order == "tree":
+        level = list(parts)
+        while len(level) > 1:
+            nxt = [oracle.merge_pair(level[i], level[i + 1]) for i in range(0, len(level) - 1, 2)]
+            if len(level) % 2:
+                nxt.append(level[-1])
+            level = nxt
+        st = level[0]
+    else:
+        perm = np.random.default_rng(19).permutation(len(parts))
+        st = fold_left([parts[i] for i in perm])
+    assert np.max(np.abs(finish(st) - ref)) <= TOL
+
+
+def test_merge_with_empty_is_identity_bit_exact():
+    d = 16
+    x = oracle.split_partials(gauss(20, d), gauss(21, 50, d), gauss(22, 50, d), 0.25, 1)[0]
+    e = oracle.empty_partial(d)
+    for y in (oracle.merge_pair(x, e), oracle.merge_pair(e, x)):
+        assert y[0] == x[0] and y[1] == x[1]
+        assert np.array_equal(y[2], x[2])
+    z = oracle.merge_pair(e, e)
+    assert z[0] == -np.inf and z[1] == 0.0 and not np.any(z[2])
+    # all-empty array merge gives the no-key convention, 0, and no NaN
+    out = oracle.merge_partials(np.full(3, -np.inf), np.zeros(3), np.zeros((3, d)))
+    assert np.array_equal(out, np.zeros(d))
+
+
+def test_merge_two_states_closed_form():
+    """Two single-key states: the merged output must be the two-key softmax."""
+    s0, s1 = 3.7, -1.2
+    v0, v1 = gauss(23, 4), gauss(24, 4)
+    a = (s0, 1.0, v0.copy())
+    b = (s1, 1.0, v1.copy())
+    sig = 1 / (1 + math.exp(-(s0 - s1)))
+    expect = v1 + (v0 - v1) * sig
+    assert np.max(np.abs(finish(oracle.merge_pair(a, b)) - expect)) <= 1e-14
+
+
+# --- the definition itself -------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_rows_sum_to_one(causal):
+    n, d = 300, 32
+    q, k = gauss(25, n, d) * 2, gauss(26, n, d)
+    P = oracle.softmax_probabilities(q, k, 0.2, causal)
+    assert np.max(np.abs(P.sum(1) - 1.0)) <= TOL
+    if causal:
+        assert np.all(P[np.triu_indices(n, 1)] == 0.0)
+    v = gauss(27, n, d)
+    assert np.max(np.abs(P @ v - one_head(q, k, v, 0.2, causal))) <= TOL
+
+
+def test_single_key_returns_its_value_row_bit_exact():
+    d = 64
+    q, k, v = gauss(28, 1, d), gauss(29, 1, d), gauss(30, 1, d)
+    assert np.array_equal(one_head(q, k, v, 0.125, causal=False), v)
+    qn, kn, vn = gauss(31, 9, d), gauss(32, 9, d), gauss(33, 9, d)
+    assert np.array_equal(one_head(qn, kn, vn, 0.125, causal=True)[0], vn[0])
+    kc = np.full((1, 1, 5, d), np.nan); vc = np.full((1, 1, 5, d), np.nan)
+    kc[0, 0, 0], vc[0, 0, 0] = kn[0], vn[0]
+    out = oracle.decode(qn[:1][None], kc, vc, [1], 0.125)
+    assert np.array_equal(out[0, 0], vn[0])
+
+
+def test_zero_query_gives_prefix_means():
+    """Q = 0 makes every visible key equally likely: row i of causal attention is
+    the mean of V rows 0..i, which pins the diagonal of the mask."""
+    n, d = 200, 16
+    q = np.zeros((n, d)); k, v = gauss(34, n, d), gauss(35, n, d)
+    expect = np.cumsum(v, axis=0) / np.arange(1, n + 1)[:, None]
+    assert np.max(np.abs(one_head(q, k, v, 0.3, causal=True) - expect)) <= TOL
+    assert np.max(np.abs(one_head(q, k, v, 0.3, causal=False) - v.mean(0))) <= TOL
+
+
+def test_equal_keys_give_mean_of_values():
+    n, d = 123, 16
+    q = gauss(36, 10, d) * 5
+    k = np.repeat(gauss(37, 1, d), n, axis=0)
+    v = gauss(38, n, d)
+    assert np.max(np.abs(one_head(q, k, v, 0.3, causal=False) - v.mean(0))) <= TOL
+
+
+def test_two_keys_closed_form():
+    d = 32
+    q, k, v = gauss(39, 1, d), gauss(40, 2, d), gauss(41, 2, d)
+    scale = 0.17
+    s0, s1 = scale * q[0] @ k[0], scale * q[0] @ k[1]
+    expect = v[1] + (v[0] - v[1]) / (1 + math.exp(-(s0 - s1)))
+    assert np.max(np.abs(one_head(q, k, v, scale, causal=False)[0] - expect)) <= 1e-14
+
+
+def test_constant_values_are_returned_unchanged():
+    n, d = 150, 8
+    c = gauss(42, d)
+    out = one_head(gauss(43, n, d) * 4, gauss(44, n, d), np.tile(c, (n, 1)), 0.5, causal=True)
+    assert np.max(np.abs(out - c)) <= TOL
+
+
+def test_permuting_keys_with_values_changes_nothing():
+    n, d = 97, 16
+    q, k, v = gauss(45, 20, d), gauss(46, n, d), gauss(47, n, d)
+    perm = np.random.default_rng(48).permutation(n)
+    a = one_head(q, k, v, 0.25, causal=False)
+    b = one_head(q, k[perm], v[perm], 0.25, causal=False)
+    assert np.max(np.abs(a - b)) <= TOL
+
+
+def test_gqa_index_arithmetic_equals_repeat_interleave_bit_exact():
+    """'GQA in the kernel': query head i reads KV head i // (h/h_kv); the copy
+    made by repeat_interleave is the same computation."""
+    B, hq, hkv, n, d = 2, 8, 2, 33, 16
+    q, k, v = gauss(49, B, hq, n, d), gauss(50, B, hkv, n, d), gauss(51, B, hkv, n, d)
+    a = oracle.attention(q, k, v, 0.25, causal=True)
+    kx = np.repeat(k, hq // hkv, axis=1)
+    vx = np.repeat(v, hq // hkv, axis=1)
+    b = oracle.attention(q, kx, vx, 0.25, causal=True)
+    assert np.array_equal(a, b)
+    # and head 1 really does read KV head 0 (not head 1 mod 2)
+    assert oracle.kv_head_of(1, hq, hkv) == 0 and oracle.kv_head_of(4, hq, hkv) == 1
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_matches_torch_sdpa_fp64(causal):
+    B, hq, hkv, n, d = 2, 4, 2, 70, 32
+    q, k, v = gauss(52, B, hq, n, d), gauss(53, B, hkv, n, d), gauss(54, B, hkv, n, d)
+    scale = 1 / math.sqrt(d)
+    ours = oracle.attention(q, k, v, scale, causal)
+    tq = torch.from_numpy(q)
+    tk = torch.from_numpy(k).repeat_interleave(hq // hkv, dim=1)
+    tv = torch.from_numpy(v).repeat_interleave(hq // hkv, dim=1)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale)
+    assert np.max(np.abs(ours - ref.numpy())) <= TOL
+
+
+def test_decode_matches_sdpa_and_ignores_rows_past_length():
+    B, hq, hkv, L, d = 3, 8, 2, 40, 16
+    lens = [40, 1, 17]
+    q = gauss(55, B, hq, d)
+    kc, vc = gauss(56, B, hkv, L, d), gauss(57, B, hkv, L, d)
+    for b, n in enumerate(lens):
+        kc[b, :, n:] = np.nan
+        vc[b, :, n:] = np.nan
+    out = oracle.decode(q, kc, vc, lens, 0.25)
+    assert np.all(np.isfinite(out))
+    for b, n in enumerate(lens):
+        tk = torch.from_numpy(kc[b, :, :n]).repeat_interleave(hq // hkv, dim=0)
+        tv = torch.from_numpy(vc[b, :, :n]).repeat_interleave(hq // hkv, dim=0)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[b])[:, None], tk, tv, scale=0.25)[:, 0]
+        assert np.max(np.abs(out[b] - ref.numpy())) <= TOL
+
+
+def test_decode_is_the_last_row_of_causal_prefill():
+    n, d = 64, 16
+    q, k, v = gauss(58, n, d), gauss(59, n, d), gauss(60, n, d)
+    pre = one_head(q, k, v, 0.25, causal=True)
+    for L in (1, 2, 33, 64):
+        dec = oracle.decode(q[L - 1][None, None], k[None, None], v[None, None], [L], 0.25)
+        assert np.max(np.abs(dec[0, 0] - one_head(q[:L], k[:L], v[:L], 0.25, causal=True)[L - 1])) <= TOL
+    assert np.max(np.abs(oracle.decode(q[-1][None, None], k[None, None], v[None, None], [n], 0.25)[0, 0]
+                         - pre[-1])) <= TOL
+
+
+def test_decode_with_no_keys_is_zero():
+    out = oracle.decode(gauss(61, 1, 2, 8), np.full((1, 1, 4, 8), np.nan), np.full((1, 1, 4, 8), np.nan),
+                        [0], 0.3)
+    assert np.array_equal(out, np.zeros((1, 2, 8)))
+
+
+def test_attention_rows_matches_full_output():
+    B, hq, n, d = 1, 2, 130, 32
+    q, k, v = gauss(62, B, hq, n, d), gauss(63, B, hq, n, d), gauss(64, B, hq, n, d)
+    full = oracle.attention(q, k, v, 0.2, causal=True)
+    rows = np.array([0, 1, 63, 64, 129])
+    part = oracle.attention_rows(q[0, 1, rows], k[0, 1], v[0, 1], 0.2, rows)
+    assert np.max(np.abs(part - full[0, 1, rows])) <= TOL
+
+
+# --- range: why max subtraction is required ---------------------------------------------
+
+def test_fp16_exp_overflow_threshold():
+    g = GOLDEN["fp16_exp_overflow"]
+    x = oracle.fp16_exp_overflow_threshold()
+    assert round(x, 1) == g["printed_threshold"]
+    assert math.isclose(math.exp(x), g["largest_fp16"], rel_tol=1e-12)
+    assert float(torch.tensor(math.exp(x + 0.01)).half()) == math.inf
+    assert float(torch.tensor(math.exp(x - 0.01)).half()) < math.inf
+
+
+def test_ragged_decode_recipe_exceeds_fp16_exp_range():
+    """The ×8 query of the ragged-decode workload drives scaled scores past
+    ln(65504); the oracle still returns finite outputs because it subtracts the max."""
+    w = workloads.WORKLOADS["decode_ragged_b64_hq64_hkv8_d128_len1024to32768_q8_bf16"]
+    q, k, v, lens = workloads.decode_inputs(w, batch=2, max_kv_len=1024)
+    qf, kf = q.double().numpy(), k.double().numpy()
+    g = w.hq // w.hkv
+    smax = max(float((w.scale * kf[b, h // g] @ qf[b, h]).max()) for b in range(2) for h in range(w.hq))
+    assert smax > oracle.fp16_exp_overflow_threshold()
+    out = oracle.decode(qf, kf, v.double().numpy(), lens.numpy(), w.scale)
+    assert np.all(np.isfinite(out))
