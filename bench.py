@@ -1,0 +1,323 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+One step is one pass of the whole path over synthetic inputs already resident
+in HBM:
+
+* prefill forward on the non-causal batch-4, 32-head, N=4096 bf16 workload at
+  d=64 and at d=128 (``attn_prefill_fwd``), and
+* single-query split-K decode over one sequence's 262144-position bf16 cache
+  with 32 query / 8 KV heads, d=128 (``attn_decode_splitk`` then
+  ``attn_merge_partials``).
+
+The prefill and decode halves are timed as two separately synchronised regions
+of K steps each (wall clock, ``torch.cuda.synchronize`` on both sides), after W
+untimed warm-up steps.  ``value`` is the prefill throughput in algorithmic
+TFLOP/s (4·d FLOPs per visible query-key pair); the decode throughput in
+algorithmic KV GB/s (every K and V byte read once) is reported beside it.  Each
+kernel's average launch duration is taken with HIP events recorded on the
+stream the kernels are launched on; the ``roofline`` object is for the
+dominant (longest-running) kernel, ``kernels`` lists all of them.  Inputs
+alternate between two copies so no launch finds the previous one's data in the
+last-level cache.
+
+``cpu_baseline`` times the fp64 oracle on a bounded sample of the same prefill
+workload (whole heads until about ``--cpu-seconds`` have passed), on the host
+cores, as a reported baseline only.
+
+Prints exactly one JSON line on stdout.  Only one GPU is supported.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "prefill TFLOP/s and decode KV GB/s on 1 MI355X, each as % of roofline"
+PEAK_MFMA_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E peak
+PREFILL = ["prefill_b4_h32_n4096_d64_bf16", "prefill_b4_h32_n4096_d128_bf16"]
+DECODE = "decode_b1_hq32_hkv8_d128_len262144_bf16"
+CSRC = os.path.join(ROOT, "exact_attention_flashattention_amd", "csrc")
+KERNEL_SOURCES = {
+    "prefill_fwd_kernel": ["prefill_fwd.hip", "device_common.hpp"],
+    "decode_splitk_kernel": ["decode_splitk.hip", "device_common.hpp"],
+    "merge_partials_kernel": ["merge_partials.hip", "device_common.hpp"],
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(label: str, kernel: str):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE counts,
+    if they were taken on the current source of the kernel; else None."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh).get("kernels", {}).get(label)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != source_sha(kernel):
+        return None
+    return rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(inputs, w, seconds: float):
+    """The oracle, untuned, on whole heads of the d=128 prefill workload until
+    ``seconds`` of CPU time have passed."""
+    import numpy as np
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"),
+                      default=1)
+    except Exception:  # pragma: no cover
+        threads = 1
+    q, k, v = inputs
+    g = w.hq // w.hkv
+    done, flops, elapsed = 0, 0.0, 0.0
+    per_head = 4.0 * w.d * w.n * w.n
+    for b in range(w.batch):
+        for h in range(w.hq):
+            qh = q[b, h].float().cpu().double().numpy()
+            kh = k[b, h // g].float().cpu().double().numpy()
+            vh = v[b, h // g].float().cpu().double().numpy()
+            t0 = time.perf_counter()
+            oracle.attention(qh[None, None], kh[None, None], vh[None, None], w.scale, w.causal)
+            elapsed += time.perf_counter() - t0
+            done += 1
+            flops += per_head
+            if elapsed >= seconds:
+                break
+        if elapsed >= seconds:
+            break
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {w.batch * w.hq} (batch, head) slices of {w.name}, whole rows, fp64 numpy; "
+                      f"{elapsed:.1f} s; host {cpu_model()}, {os.cpu_count()} logical CPUs"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["all", "prefill_d64", "prefill_d128", "decode"], default="all",
+                    help="run only one kernel family (for profiler runs)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="instead of the bench, run plain device copies of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on exactly one GPU: this build has no multi-GPU path (asked for --gpus "
+              f"{args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import exact_attention_flashattention_amd as A
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    A._lib.load()
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {args.copy_calibration_mib} MiB x {max(1, args.steps)}")
+        return 0
+
+    stream = torch.cuda.current_stream(dev)
+    K, W = args.steps, args.warmup
+    run_prefill = [n for n in PREFILL if args.only in ("all", "prefill_d" + n.split("_d")[1].split("_")[0])]
+    run_decode = args.only in ("all", "decode")
+
+    # ---- inputs (two copies each), outputs and workspaces: all allocated before timing
+    pre = []
+    for name in run_prefill:
+        w = workloads.WORKLOADS[name]
+        copies = [workloads.prefill_inputs(w, device=dev, salt=s) for s in (0, 1)]
+        outs = [torch.empty_like(c[0]) for c in copies]
+        pre.append((w, copies, outs))
+    dec = None
+    if run_decode:
+        w = workloads.WORKLOADS[DECODE]
+        copies = []
+        for s in (0, 1):
+            q, kc, vc, lens = workloads.decode_inputs(w, device=dev, salt=s)
+            copies.append((q, kc, vc, lens.to(dev)))
+        S = A.decode_num_splits(w.batch, w.hkv, w.max_kv_len)
+        part = (torch.empty((w.batch, w.hq, S), dtype=torch.float32, device=dev),
+                torch.empty((w.batch, w.hq, S), dtype=torch.float32, device=dev),
+                torch.empty((w.batch, w.hq, S, w.d), dtype=torch.float32, device=dev))
+        out = torch.empty((w.batch, w.hq, w.d), dtype=torch.bfloat16, device=dev)
+        total_len = int(sum(int(c[3].sum()) for c in copies[:1]))
+        dec = (w, copies, S, part, out, total_len)
+    torch.cuda.synchronize()
+
+    def prefill_step(i, ev=None):
+        for j, (w, copies, outs) in enumerate(pre):
+            q, k, v = copies[i % 2]
+            if ev is not None:
+                ev[j][0].record(stream)
+            A.prefill_fwd(q, k, v, causal=w.causal, scale=w.scale, out=outs[i % 2])
+            if ev is not None:
+                ev[j][1].record(stream)
+
+    def decode_step(i, ev=None):
+        w, copies, S, part, out, _ = dec
+        q, kc, vc, lens = copies[i % 2]
+        if ev is not None:
+            ev[0].record(stream)
+        A.decode_splitk(q, kc, vc, lens, S, w.scale, partials=part)
+        if ev is not None:
+            ev[1].record(stream)
+        A.merge_partials(*part, torch.bfloat16, out=out)
+        if ev is not None:
+            ev[2].record(stream)
+
+    def events(n):
+        return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+    result_kernels = []
+    pre_wall = dec_wall = 0.0
+    pre_flops = sum(w.flops() for w, _, _ in pre)
+
+    # ---- prefill region
+    if pre:
+        for i in range(W):
+            prefill_step(i)
+        torch.cuda.synchronize()
+        ev = [[events(2) for _ in pre] for _ in range(K)]
+        t0 = time.perf_counter()
+        for i in range(K):
+            prefill_step(i, ev[i])
+        torch.cuda.synchronize()
+        pre_wall = time.perf_counter() - t0
+        for j, (w, _, outs) in enumerate(pre):
+            ms = sum(ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(K)) / K
+            tflops = w.flops() / (ms * 1e-3) / 1e12
+            if not torch.isfinite(outs[0]).all():
+                raise RuntimeError(f"non-finite prefill output on {w.name}")
+            label = f"prefill_fwd_kernel<bf16,d{w.d},{'causal' if w.causal else 'noncausal'}>"
+            traffic = measured_traffic(label, "prefill_fwd_kernel")
+            result_kernels.append({
+                "kernel": label, "workload": w.name, "avg_ms": ms, "bound": "mfma", "achieved": tflops,
+                "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s", "frac": tflops / PEAK_MFMA_BF16_TFLOPS,
+                "traffic": traffic, "algorithmic_flops": w.flops(), "compulsory_bytes": w.io_bytes()})
+
+    # ---- decode region
+    if dec:
+        w, copies, S, part, out, total_len = dec
+        for i in range(W):
+            decode_step(i)
+        torch.cuda.synchronize()
+        ev = [events(3) for _ in range(K)]
+        t0 = time.perf_counter()
+        for i in range(K):
+            decode_step(i, ev[i])
+        torch.cuda.synchronize()
+        dec_wall = time.perf_counter() - t0
+        if not torch.isfinite(out).all():
+            raise RuntimeError("non-finite decode output")
+        kv_bytes = w.kv_bytes(total_len)
+        ms_split = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+        ms_merge = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+        gbs = kv_bytes / (ms_split * 1e-3) / 1e9
+        result_kernels.append({
+            "kernel": "decode_splitk_kernel<bf16,d128>", "workload": w.name, "avg_ms": ms_split, "bound": "hbm",
+            "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+            "traffic": measured_traffic("decode_splitk_kernel<bf16,d128>", "decode_splitk_kernel"),
+            "algorithmic_bytes": kv_bytes, "num_splits": S,
+            "chunk": A.decode_chunk_len(w.max_kv_len, S)})
+        part_bytes = 2.0 * w.batch * w.hq * S * (w.d + 2) * 4
+        result_kernels.append({
+            "kernel": "merge_partials_kernel<bf16,d128>", "workload": w.name, "avg_ms": ms_merge, "bound": "hbm",
+            "achieved": part_bytes / 2 / (ms_merge * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": part_bytes / 2 / (ms_merge * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "traffic": measured_traffic("merge_partials_kernel<bf16,d128>", "merge_partials_kernel"),
+            "algorithmic_bytes": part_bytes / 2})
+
+    dominant = max(result_kernels, key=lambda r: r["avg_ms"])
+    roofline = {k: dominant[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
+    roofline["kernel"] = dominant["kernel"]
+
+    value = pre_flops * K / pre_wall / 1e12 if pre else None
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": (pre_wall + dec_wall) / K * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": " + ".join([w.name for w, _, _ in pre] + ([dec[0].name] if dec else [])),
+            "prefill": [{"workload": w.name, "batch": w.batch, "hq": w.hq, "hkv": w.hkv, "n": w.n, "d": w.d,
+                         "causal": w.causal} for w, _, _ in pre],
+            "decode": ({"workload": dec[0].name, "batch": dec[0].batch, "hq": dec[0].hq, "hkv": dec[0].hkv,
+                        "d": dec[0].d, "kv_len": dec[0].max_kv_len, "num_splits": dec[2]} if dec else None),
+        },
+        "prefill_frac_of_mfma_peak": (value / PEAK_MFMA_BF16_TFLOPS) if value else None,
+        "decode": ({"value": dec[0].kv_bytes(dec[5]) * K / dec_wall / 1e9, "unit": "GB/s",
+                    "frac_of_hbm_peak": dec[0].kv_bytes(dec[5]) * K / dec_wall / 1e9 / PEAK_HBM_GBS,
+                    "timed": "attn_decode_splitk + attn_merge_partials, wall clock"} if dec else None),
+        "roofline": roofline,
+        "kernels": result_kernels,
+    }
+
+    if pre and not args.no_cpu_baseline:
+        w, copies, _ = pre[-1]
+        line["cpu_baseline"] = cpu_baseline(copies[0], w, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,118 @@
+// C ABI of libattn.so (declared in include/attn.h): argument validation on
+// the host, split planning for decode, and dispatch to the kernel launchers.
+// Nothing here allocates, frees or synchronises device memory.
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+
+#include "attn.h"
+#include "launchers.hpp"
+
+namespace {
+
+constexpr long long kMaxElems = 1LL << 40;  // per-tensor element bound the kernels' 64-bit offsets assume
+constexpr int kDecodeTargetWaves = 2048;    // decode waves that fill 256 CUs at 8 waves per CU
+constexpr int kDecodeMinChunk = 256;        // fewest keys worth a split of its own
+constexpr int kChunkAlign = 64;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool dtype_ok(int t) { return t == ATTN_F16 || t == ATTN_BF16; }
+bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
+
+attn_status from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH; }
+
+// An optional override of the split heuristic for A/B measurements:
+// ATTN_DECODE_TARGET_WAVES=<n> changes the wave count the heuristic aims for.
+int decode_target_waves() {
+  static const int v = [] {
+    const char* s = std::getenv("ATTN_DECODE_TARGET_WAVES");
+    const long x = s ? std::strtol(s, nullptr, 10) : 0;
+    return (x > 0 && x < (1L << 24)) ? (int)x : kDecodeTargetWaves;
+  }();
+  return v;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL_PTR: return "a required pointer is NULL";
+    case ATTN_ERR_BAD_SHAPE: return "bad shape or scale";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported head dimension or element type";
+    case ATTN_ERR_MISALIGNED: return "tensor pointer not 16-byte aligned";
+    case ATTN_ERR_LAUNCH: return "kernel launch failed";
+    case ATTN_ERR_TOO_LARGE: return "size beyond the kernels' index range";
+    default: return "unknown status";
+  }
+}
+
+attn_status attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, int dtype, int batch, int hq,
+                             int hkv, int n, int d, float scale, int causal, void* stream) {
+  if (!q || !k || !v || !o) return ATTN_ERR_NULL_PTR;
+  if (batch < 1 || hq < 1 || hkv < 1 || n < 1 || hq % hkv != 0 || !scale_ok(scale)) return ATTN_ERR_BAD_SHAPE;
+  if ((d != 64 && d != 128) || !dtype_ok(dtype)) return ATTN_ERR_UNSUPPORTED;
+  if ((long long)batch * hq * n * d >= kMaxElems || (long long)n * d >= (1LL << 31)) return ATTN_ERR_TOO_LARGE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_MISALIGNED;
+  return from_hip(attn::launch_prefill(q, k, v, o, dtype == ATTN_BF16, batch, hq, hkv, n, d, scale, causal != 0,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int attn_decode_num_splits(int batch, int hkv, int max_kv_len) {
+  if (batch < 1 || hkv < 1 || max_kv_len < 1) return 1;
+  const long long heads = (long long)batch * hkv;
+  const long long want = (decode_target_waves() + heads - 1) / heads;
+  const long long useful = (max_kv_len + kDecodeMinChunk - 1) / kDecodeMinChunk;
+  long long s = want < useful ? want : useful;
+  if (s < 1) s = 1;
+  if (s > 65535) s = 65535;
+  return (int)s;
+}
+
+int attn_decode_chunk_len(int max_kv_len, int num_splits) {
+  if (max_kv_len < 1 || num_splits < 1) return 0;
+  long long c = ((long long)max_kv_len + num_splits - 1) / num_splits;
+  c = (c + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
+  return (int)c;
+}
+
+size_t attn_decode_workspace_bytes(int batch, int hq, int d, int num_splits) {
+  if (batch < 1 || hq < 1 || d < 1 || num_splits < 1) return 0;
+  return (size_t)batch * hq * num_splits * (size_t)(d + 2) * sizeof(float);
+}
+
+attn_status attn_decode_splitk(const void* q, const void* k_cache, const void* v_cache, const int* kv_lens,
+                               int max_kv_len, int dtype, int batch, int hq, int hkv, int d, float scale,
+                               int num_splits, float* part_m, float* part_l, float* part_o, void* stream) {
+  if (!q || !k_cache || !v_cache || !kv_lens || !part_m || !part_l || !part_o) return ATTN_ERR_NULL_PTR;
+  if (batch < 1 || hq < 1 || hkv < 1 || max_kv_len < 1 || num_splits < 1 || hq % hkv != 0 || !scale_ok(scale))
+    return ATTN_ERR_BAD_SHAPE;
+  if ((d != 64 && d != 128) || !dtype_ok(dtype)) return ATTN_ERR_UNSUPPORTED;
+  const int groups = (hq / hkv + 15) / 16;
+  if ((long long)batch * hkv * max_kv_len * d >= kMaxElems || (long long)max_kv_len * d >= (1LL << 31) ||
+      batch > 65535 || (long long)hkv * groups > 65535 || num_splits > 65535 ||
+      (long long)batch * hq * num_splits * d >= kMaxElems)
+    return ATTN_ERR_TOO_LARGE;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(part_o))
+    return ATTN_ERR_MISALIGNED;
+  const int chunk = attn_decode_chunk_len(max_kv_len, num_splits);
+  return from_hip(attn::launch_decode_splitk(q, k_cache, v_cache, kv_lens, max_kv_len, dtype == ATTN_BF16, batch, hq,
+                                             hkv, d, scale, num_splits, chunk, part_m, part_l, part_o,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+attn_status attn_merge_partials(const float* part_m, const float* part_l, const float* part_o, int batch, int hq,
+                                int d, int num_splits, void* o, int out_dtype, void* stream) {
+  if (!part_m || !part_l || !part_o || !o) return ATTN_ERR_NULL_PTR;
+  if (batch < 1 || hq < 1 || num_splits < 1) return ATTN_ERR_BAD_SHAPE;
+  if ((d != 64 && d != 128) || !dtype_ok(out_dtype)) return ATTN_ERR_UNSUPPORTED;
+  if ((long long)batch * hq >= (1LL << 31) || (long long)batch * hq * num_splits * d >= kMaxElems)
+    return ATTN_ERR_TOO_LARGE;
+  if (!aligned16(part_o) || !aligned16(o)) return ATTN_ERR_MISALIGNED;
+  return from_hip(attn::launch_merge(part_m, part_l, part_o, batch * hq, d, num_splits, out_dtype == ATTN_BF16, o,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

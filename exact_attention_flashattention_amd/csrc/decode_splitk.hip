@@ -1,0 +1,230 @@
+// Split-K single-query decode: partial (m, l, o) states per slice of the KV
+// cache ("Flash-Decoding": the cache sequence is split across workgroups so
+// one query per sequence still fills the GPU -- "Prefill and decode are
+// different problems" on "Attention from the kernel's side", and "The four
+// attention kernels you actually use" in section 5 of "Attention Computation
+// in Practice").  The partials are merged by merge_partials.hip.
+//
+// Work decomposition: one wavefront per (split, KV head, query group,
+// sequence).  A query group is up to 16 of the g = hq/hkv query heads that
+// share the KV head, so every K/V byte the wave streams is used by all of
+// them (GQA reuse, "GQA in the kernel").  The wave walks its slice 32 keys at
+// a time; the next 32 keys' K and V rows are already in flight (16-byte
+// global loads into registers) while the current ones are used:
+//
+//   scores   Sᵀ[32 keys × 16 queries] = K·Qᵀ on 16x16x32 MFMA, K straight
+//            from its registers, Q resident in registers;
+//   softmax  running max / sum per query column, rescale by exp2(m − m_new)
+//            (the online recurrence of "The online softmax"), scores held in
+//            the exp2 domain (scale·log2 e folded into one FMA);
+//   values   V rows go to a wave-private LDS buffer and come back through the
+//            LDS transpose read as the k-major A operand of
+//            Oᵀ[D × 16] += Vᵀ·Pᵀ, P rounded to the storage type.
+//
+// The kernel is bound by HBM reads of K and V; the matrix cores and the
+// softmax arithmetic are far below their limits at g <= 16.
+#include "device_common.hpp"
+#include "launchers.hpp"
+
+namespace attn {
+
+namespace {
+
+constexpr int kStep = 32;  // keys per step
+
+template <int D>
+struct DecodeStage {
+  static constexpr int KK = D / 32;        // 16x16x32 k-steps over the head dimension
+  static constexpr int VCH = D / 16;       // 16-byte V chunks per lane per step (32 rows · D/8 chunks / 64)
+  u32x4 k[2][KK];                          // [key subtile][k-step]
+  u32x4 v[VCH];
+};
+
+}  // namespace
+
+template <class T, int D>
+__global__ __launch_bounds__(64) void decode_splitk_kernel(const char* __restrict__ q, const char* __restrict__ kc,
+                                                           const char* __restrict__ vc,
+                                                           const int* __restrict__ kv_lens, int max_kv_len, int hq,
+                                                           int hkv, int g, int chunk, int num_splits, float c,
+                                                           float* __restrict__ part_m, float* __restrict__ part_l,
+                                                           float* __restrict__ part_o) {
+  constexpr int KK = D / 32;
+  constexpr int DT = D / 16;              // 16-row output tiles of the head dimension
+  constexpr int VCH = D / 16;
+  constexpr int VP = 2 * D + 64;          // LDS pitch of a V row in bytes (bank-spread for the transpose read)
+  constexpr int CPR = D / 8;              // 16-byte chunks per K/V row
+  __shared__ __attribute__((aligned(16))) char vlds[kStep * VP];
+
+  const int lane = threadIdx.x;
+  const int r = lane & 15;                // MFMA column: query within the group / row within a tile
+  const int grp = lane >> 4;              // lane group 0..3
+  const int split = blockIdx.x;
+  const int kh = blockIdx.y % hkv;
+  const int qgrp = blockIdx.y / hkv;
+  const int b = blockIdx.z;
+  const int qi = qgrp * 16 + r;           // query index within the KV head's group
+  const bool qvalid = qi < g;
+  const int h = kh * g + (qvalid ? qi : 0);
+
+  int kv_len = kv_lens[b];
+  kv_len = kv_len < 0 ? 0 : (kv_len > max_kv_len ? max_kv_len : kv_len);
+  const int start = split * chunk;
+  const int end = min(start + chunk, kv_len);
+
+  const size_t prow = ((size_t)b * hq + h) * num_splits + split;
+  float* po = part_o + prow * D;
+
+  if (start >= end) {  // no keys in this slice: the empty state (-inf, 0, 0)
+    if (qvalid) {
+      if (grp == 0) {
+        part_m[prow] = kNegInf;
+        part_l[prow] = 0.f;
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16 + 4 * grp) = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    return;
+  }
+
+  // Q operand (B of Sᵀ = K·Qᵀ): lane (query r, group grp) holds d-chunk 4·kk + grp.
+  u32x4 qf[KK];
+  {
+    const char* qp = q + ((size_t)b * hq + h) * D * 2;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) qf[kk] = qvalid ? gload16(qp + (4 * kk + grp) * 16) : zero4();
+  }
+
+  const size_t head_base = ((size_t)b * hkv + kh) * (size_t)max_kv_len * D * 2;
+  const char* kbase = kc + head_base;
+  const char* vbase = vc + head_base;
+
+  auto load = [&](DecodeStage<D>& st, int k0) {
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      const int key = k0 + sb * 16 + r;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        st.k[sb][kk] = key < end ? gload16(kbase + (size_t)key * D * 2 + (4 * kk + grp) * 16) : zero4();
+    }
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+      const int cidx = lane + 64 * i;
+      const int key = k0 + cidx / CPR;
+      st.v[i] = key < end ? gload16(vbase + (size_t)key * D * 2 + (cidx % CPR) * 16) : zero4();
+    }
+  };
+
+  float m_run = kNegInf, l_run = 0.f;
+  f32x4 oacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto process = [&](const DecodeStage<D>& st, int k0) {
+    __syncthreads();  // previous step's transpose reads are done with the buffer
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+      const int cidx = lane + 64 * i;
+      lds_write16(vlds, (cidx / CPR) * VP + (cidx % CPR) * 16, st.v[i]);
+    }
+    // scores: s[sb][e] is key k0 + 16·sb + 4·grp + e against query column r
+    f32x4 s[2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      s[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) s[sb] = T::mfma16(st.k[sb][kk], qf[kk], s[sb]);
+    }
+    if (k0 + kStep > end) {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (k0 + sb * 16 + 4 * grp + e >= end) s[sb][e] = kNegInf;
+    }
+    float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    mx = max_xor32(max_xor16(mx));
+    // every processed step holds at least one live key, so m_new is finite
+    const float m_new = fmaxf(m_run, mx * c);
+    const float alpha = fast_exp2(m_run - m_new);  // 0 on the first step (m_run = -inf)
+    float psum = 0.f;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p = fast_exp2(fmaf(s[sb][e], c, -m_new));
+        s[sb][e] = p;
+        psum += p;
+      }
+    l_run = fmaf(l_run, alpha, psum);
+    m_run = m_new;
+    const u32x4 pf = {T::pack2(s[0][0], s[0][1]), T::pack2(s[0][2], s[0][3]), T::pack2(s[1][0], s[1][1]),
+                      T::pack2(s[1][2], s[1][3])};
+    __syncthreads();  // V rows are in LDS
+    const uint32_t row_a = (4 * grp + (r >> 2)) * VP;
+    const uint32_t row_b = (16 + 4 * grp + (r >> 2)) * VP;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const uint32_t col = (dt * 16 + 4 * (r & 3)) * 2;
+      const u32x2 va = lds_read_tr16(vlds, row_a + col);
+      const u32x2 vb = lds_read_tr16(vlds, row_b + col);
+      oacc[dt] = T::mfma16(u32x4{va[0], va[1], vb[0], vb[1]}, pf, oacc[dt] * alpha);
+    }
+  };
+
+  DecodeStage<D> A, B;
+  load(A, start);
+  for (int k0 = start;; k0 += 2 * kStep) {
+    const bool more1 = k0 + kStep < end;
+    if (more1) load(B, k0 + kStep);
+    process(A, k0);
+    if (!more1) break;
+    const bool more2 = k0 + 2 * kStep < end;
+    if (more2) load(A, k0 + 2 * kStep);
+    process(B, k0 + kStep);
+    if (!more2) break;
+  }
+
+  // partial state of this slice, natural-log units
+  const float l_tot = sum_xor32(sum_xor16(l_run));
+  if (qvalid) {
+    if (grp == 0) {
+      part_m[prow] = m_run * kLn2;
+      part_l[prow] = l_tot;
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16 + 4 * grp) = oacc[dt];
+  }
+}
+
+template <class T, int D>
+static hipError_t launch_decode_t(const void* q, const void* kc, const void* vc, const int* kv_lens, int max_kv_len,
+                                  int batch, int hq, int hkv, float scale, int num_splits, int chunk, float* pm,
+                                  float* pl, float* po, hipStream_t stream) {
+  const int g = hq / hkv;
+  const int groups = (g + 15) / 16;
+  dim3 grid(num_splits, hkv * groups, batch);
+  decode_splitk_kernel<T, D><<<grid, dim3(64), 0, stream>>>(
+      static_cast<const char*>(q), static_cast<const char*>(kc), static_cast<const char*>(vc), kv_lens, max_kv_len,
+      hq, hkv, g, chunk, num_splits, scale * kLog2e, pm, pl, po);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_splitk(const void* q, const void* k_cache, const void* v_cache, const int* kv_lens,
+                                int max_kv_len, bool bf16, int batch, int hq, int hkv, int d, float scale,
+                                int num_splits, int chunk, float* part_m, float* part_l, float* part_o,
+                                hipStream_t stream) {
+  if (bf16) {
+    return d == 64 ? launch_decode_t<Bf16, 64>(q, k_cache, v_cache, kv_lens, max_kv_len, batch, hq, hkv, scale,
+                                               num_splits, chunk, part_m, part_l, part_o, stream)
+                   : launch_decode_t<Bf16, 128>(q, k_cache, v_cache, kv_lens, max_kv_len, batch, hq, hkv, scale,
+                                                num_splits, chunk, part_m, part_l, part_o, stream);
+  }
+  return d == 64 ? launch_decode_t<F16, 64>(q, k_cache, v_cache, kv_lens, max_kv_len, batch, hq, hkv, scale,
+                                            num_splits, chunk, part_m, part_l, part_o, stream)
+                 : launch_decode_t<F16, 128>(q, k_cache, v_cache, kv_lens, max_kv_len, batch, hq, hkv, scale,
+                                             num_splits, chunk, part_m, part_l, part_o, stream);
+}
+
+}  // namespace attn

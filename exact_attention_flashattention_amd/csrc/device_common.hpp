@@ -1,0 +1,113 @@
+// Device-side building blocks shared by the attention kernels (gfx950 only).
+//
+// Vector types, 128-bit memory access, the bf16/fp16 matrix-core (MFMA)
+// instructions used for the two contractions Q·Kᵀ and P·V, the LDS transpose
+// read used to feed V to the matrix cores, and fp32 -> bf16/fp16 rounding.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+#define ATTN_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// Storage element tags.  Both are 16-bit; they differ in the MFMA opcode and
+// in how fp32 is rounded back to storage.
+struct Bf16 {
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    bf16x2 v = {(__bf16)a, (__bf16)b};  // v_cvt_pk_bf16_f32: round to nearest even
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  static __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                   c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                   c, 0, 0, 0);
+  }
+};
+
+struct F16 {
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    f16x2 v = {(_Float16)a, (_Float16)b};  // v_cvt_f16_f32: round to nearest even
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  static __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                  0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                  0, 0, 0);
+  }
+};
+
+__device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
+
+// 16-byte global load / store (global_load_dwordx4 / global_store_dwordx4).
+__device__ __forceinline__ u32x4 gload16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void gstore16(void* p, u32x4 x) { *reinterpret_cast<u32x4*>(p) = x; }
+__device__ __forceinline__ void gstore8(void* p, u32x2 x) { *reinterpret_cast<u32x2*>(p) = x; }
+
+// LDS access at a byte offset from an LDS base pointer.
+__device__ __forceinline__ u32x4 lds_read16(const char* base, uint32_t off) {
+  return *reinterpret_cast<const u32x4*>(base + off);
+}
+__device__ __forceinline__ void lds_write16(char* base, uint32_t off, u32x4 x) {
+  *reinterpret_cast<u32x4*>(base + off) = x;
+}
+
+// LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane j names 8 bytes: columns 4·(j%4) .. 4·(j%4)+3 of row j/4 of a 4 x 16
+// block of 16-bit elements.  Lane i of the group receives column i of that
+// block: its 4 rows, in row order.  Reading V (rows = keys, columns = head
+// dimension) this way hands each lane 4 consecutive keys of one column, which
+// is the k-major operand layout of the matrix instructions.
+__device__ __forceinline__ u32x2 lds_read_tr16(const char* base, uint32_t off) {
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4*)(base + off));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// exp2 on the transcendental unit (v_exp_f32); exp2(-inf) = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Cross-lane reductions without LDS.  v_permlane32_swap exchanges rows 2-3
+// (lanes 32..63) of its first operand with rows 0-1 (lanes 0..31) of its
+// second; given the same value twice it returns (lower half, lower half) and
+// (upper half, upper half), so combining the pair reduces lane l with lane
+// l^32 and leaves the same bits in both.  v_permlane16_swap does the same for
+// rows 1/3 against rows 0/2, pairing lane l with lane l^16.
+__device__ __forceinline__ float max_xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+}  // namespace attn

@@ -1,0 +1,21 @@
+// Internal launch entry points, one per kernel family.  Shapes and pointers
+// are validated by the C ABI layer before any of these is called; each
+// returns the HIP status of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace attn {
+
+hipError_t launch_prefill(const void* q, const void* k, const void* v, void* o, bool bf16, int batch, int hq,
+                          int hkv, int n, int d, float scale, bool causal, hipStream_t stream);
+
+hipError_t launch_decode_splitk(const void* q, const void* k_cache, const void* v_cache, const int* kv_lens,
+                                int max_kv_len, bool bf16, int batch, int hq, int hkv, int d, float scale,
+                                int num_splits, int chunk, float* part_m, float* part_l, float* part_o,
+                                hipStream_t stream);
+
+hipError_t launch_merge(const float* part_m, const float* part_l, const float* part_o, int rows, int d,
+                        int num_splits, bool bf16, void* out, hipStream_t stream);
+
+}  // namespace attn

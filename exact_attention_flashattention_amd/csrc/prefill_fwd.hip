@@ -1,0 +1,259 @@
+// Prefill forward: exact attention of a square problem, tile by tile.
+//
+// FlashAttention as described in "FlashAttention: what never touches memory"
+// ("Attention from the kernel's side") and "03 · The structure" ("Quantized
+// kernels"): a block of query rows stays resident, tiles of K and V stream
+// past it through on-chip memory, each tile's scores update the running
+// (m, l, o) of every row with the online-softmax recurrence, and O is written
+// once.  Scores and probabilities exist only in registers.
+//
+// gfx950 mapping (one workgroup = 4 wavefronts = 128 query rows):
+//   * each wave owns 32 query rows; its Q rows sit in registers as the
+//     B operand of the 32x32x16 matrix instruction;
+//   * K and V tiles of 64 keys are loaded with coalesced 16-byte global loads
+//     into registers one iteration ahead, then stored to a double-buffered
+//     LDS stage, so HBM/L2 latency hides behind the current tile's math;
+//   * scores are computed transposed, Sᵀ = K·Qᵀ, so that each lane holds 16
+//     keys of ONE query: the row max needs only an in-lane max plus one
+//     exchange between the wave's halves (v_permlane32_swap), the rescale
+//     factor is one scalar per lane, and the probabilities are already in
+//     the register layout of the B operand of Oᵀ += Vᵀ·Pᵀ (no shuffle);
+//   * V reaches the matrix cores through the LDS transpose read
+//     (ds_read_b64_tr_b16), which delivers 4 consecutive keys of one
+//     head-dimension column per lane;
+//   * the softmax runs in the exp2 domain (scale·log2 e folded into one FMA
+//     per score, v_exp_f32);
+//   * causal: key tiles wholly above a wave's diagonal are skipped, the mask
+//     is applied only on tiles that cross the diagonal or the sequence end
+//     (block classification of "Masking variants", "Attention Computation in
+//     Practice" section 5), and the heaviest query tiles are launched first.
+#include "device_common.hpp"
+#include "launchers.hpp"
+
+namespace attn {
+
+namespace {
+
+template <int D>
+struct PrefillCfg {
+  static constexpr int WAVES = 4;
+  static constexpr int BR = 32 * WAVES;       // query rows per workgroup
+  static constexpr int BC = 64;               // keys per tile
+  static constexpr int KP = 2 * D + 16;       // LDS pitch of a K row (bytes): 4-bank row skew
+  static constexpr int VP = 2 * D + 64;       // LDS pitch of a V row (bytes): 16-bank row skew
+  static constexpr int KBYTES = BC * KP;
+  static constexpr int VBYTES = BC * VP;
+  static constexpr int STAGE = KBYTES + VBYTES;
+  static constexpr int LDS = 2 * STAGE;
+  static constexpr int CPR = D / 8;           // 16-byte chunks per row
+  static constexpr int LOADS = BC * CPR / 256; // 16-byte chunks per thread per tile, each of K and V
+};
+
+}  // namespace
+
+template <class T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void prefill_fwd_kernel(const char* __restrict__ q, const char* __restrict__ k,
+                                                          const char* __restrict__ v, char* __restrict__ o, int batch,
+                                                          int hq, int hkv, int n, float c, int num_q_tiles) {
+  using Cfg = PrefillCfg<D>;
+  constexpr int KK = D / 16;  // 32x32x16 k-steps over the head dimension
+  constexpr int DT = D / 32;  // 32-row output tiles of the head dimension
+  __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5;
+
+  // work item: query heads vary fastest, then batch, then query tile
+  int id = blockIdx.x;
+  const int h = id % hq;
+  id /= hq;
+  const int b = id % batch;
+  const int t = id / batch;
+  const int qt = CAUSAL ? (num_q_tiles - 1 - t) : t;  // causal: longest rows first
+  const int kvh = h / (hq / hkv);
+
+  const int q0 = qt * Cfg::BR;
+  const int qw = q0 + wave * 32;
+  const int qrow = qw + (lane & 31);
+  const size_t qo_base = ((size_t)b * hq + h) * (size_t)n * D * 2;
+  const size_t kv_base = ((size_t)b * hkv + kvh) * (size_t)n * D * 2;
+  const char* kp = k + kv_base;
+  const char* vp = v + kv_base;
+
+  // Q operand (B of Sᵀ = K·Qᵀ): lane holds query qrow, head-dim elements kk·16 + 8·half .. +7
+  u32x4 qf[KK];
+  {
+    const char* qp = q + qo_base + (size_t)qrow * D * 2;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) qf[kk] = qrow < n ? gload16(qp + (kk * 16 + 8 * half) * 2) : zero4();
+  }
+
+  const int kend = CAUSAL ? min(n, q0 + Cfg::BR) : n;  // keys any row of this workgroup can see
+  const int nkt = (kend + Cfg::BC - 1) / Cfg::BC;
+  const int wave_last = min(n - 1, qw + 31);          // last live query row of this wave
+
+  u32x4 kst[Cfg::LOADS], vst[Cfg::LOADS];
+  auto load_tile = [&](int it) {
+    const int j0 = it * Cfg::BC;
+#pragma unroll
+    for (int i = 0; i < Cfg::LOADS; ++i) {
+      const int cidx = tid + 256 * i;
+      const int key = j0 + cidx / Cfg::CPR;
+      const size_t off = (size_t)key * D * 2 + (cidx % Cfg::CPR) * 16;
+      kst[i] = key < n ? gload16(kp + off) : zero4();
+      vst[i] = key < n ? gload16(vp + off) : zero4();
+    }
+  };
+  auto store_tile = [&](int buf) {
+    char* ks = lds + buf * Cfg::STAGE;
+    char* vs = ks + Cfg::KBYTES;
+#pragma unroll
+    for (int i = 0; i < Cfg::LOADS; ++i) {
+      const int cidx = tid + 256 * i;
+      const int row = cidx / Cfg::CPR, col = cidx % Cfg::CPR;
+      lds_write16(ks, row * Cfg::KP + col * 16, kst[i]);
+      lds_write16(vs, row * Cfg::VP + col * 16, vst[i]);
+    }
+  };
+
+  float m_run = kNegInf, l_run = 0.f;
+  f32x16 oacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[dt][e] = 0.f;
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int it = 0; it < nkt; ++it) {
+    if (it + 1 < nkt) load_tile(it + 1);
+    const int j0 = it * Cfg::BC;
+    if (!CAUSAL || j0 <= wave_last) {
+      const char* ks = lds + (it & 1) * Cfg::STAGE;
+      const char* vs = ks + Cfg::KBYTES;
+
+      // Sᵀ for two 32-key subtiles: s[sb][e] is key j0 + 32·sb + 8·(e/4) + 4·half + e%4 against query qrow
+      f32x16 s[2];
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[sb][e] = 0.f;
+        const uint32_t krow = (sb * 32 + (lane & 31)) * Cfg::KP + half * 16;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) s[sb] = T::mfma32(lds_read16(ks, krow + kk * 32), qf[kk], s[sb]);
+      }
+
+      const bool need_mask = (j0 + Cfg::BC > n) || (CAUSAL && j0 + Cfg::BC - 1 > qw);
+      if (need_mask) {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = j0 + sb * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+            if (key >= n || (CAUSAL && key > qrow)) s[sb][e] = kNegInf;
+          }
+      }
+
+      float mx = kNegInf;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[sb][e]);
+      mx = max_xor32(mx);
+      const float m_new = fmaxf(m_run, mx * c);
+      const float m_use = (m_new == kNegInf) ? 0.f : m_new;  // a row with no live key yet stays empty
+      const float alpha = fast_exp2(m_run - m_use);          // 0 while m_run = -inf
+      float psum = 0.f;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float p = fast_exp2(fmaf(s[sb][e], c, -m_use));
+          s[sb][e] = p;
+          psum += p;
+        }
+      l_run = fmaf(l_run, alpha, psum);
+      m_run = m_new;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+
+      // P as the B operand of Oᵀ += Vᵀ·Pᵀ, one 16-key k-step per (subtile, ks)
+      u32x4 pf[2][2];
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          pf[sb][ks] = u32x4{T::pack2(s[sb][8 * ks + 0], s[sb][8 * ks + 1]), T::pack2(s[sb][8 * ks + 2], s[sb][8 * ks + 3]),
+                             T::pack2(s[sb][8 * ks + 4], s[sb][8 * ks + 5]), T::pack2(s[sb][8 * ks + 6], s[sb][8 * ks + 7])};
+
+      // V operand (A of Oᵀ += Vᵀ·Pᵀ): lane (group G of 16, index j) takes head-dim column
+      // 32·dt + 16·(G&1) + j and keys 32·sb + 16·ks + 4·(G>>1) + {0..3} and the same + 8
+      const int G = lane >> 4, j = lane & 15;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const uint32_t col = (dt * 32 + 16 * (G & 1) + 4 * (j & 3)) * 2;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const uint32_t row = sb * 32 + 16 * ks + 4 * (G >> 1) + (j >> 2);
+            const u32x2 va = lds_read_tr16(vs, row * Cfg::VP + col);
+            const u32x2 vb = lds_read_tr16(vs, (row + 8) * Cfg::VP + col);
+            oacc[dt] = T::mfma32(u32x4{va[0], va[1], vb[0], vb[1]}, pf[sb][ks], oacc[dt]);
+          }
+      }
+    }
+    if (it + 1 < nkt) store_tile((it + 1) & 1);
+    __syncthreads();
+  }
+
+  // epilogue: O = o / l, rounded to the storage type, written once
+  const float l_tot = sum_xor32(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (qrow < n) {
+    char* op = o + qo_base + (size_t)qrow * D * 2;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int eh = 0; eh < 4; ++eh) {
+        const int dcol = dt * 32 + 8 * eh + 4 * half;
+        const u32x2 w = {T::pack2(oacc[dt][4 * eh + 0] * inv, oacc[dt][4 * eh + 1] * inv),
+                         T::pack2(oacc[dt][4 * eh + 2] * inv, oacc[dt][4 * eh + 3] * inv)};
+        gstore8(op + dcol * 2, w);
+      }
+  }
+}
+
+template <class T, int D, bool CAUSAL>
+static hipError_t launch_prefill_t(const void* q, const void* k, const void* v, void* o, int batch, int hq, int hkv,
+                                   int n, float scale, hipStream_t stream) {
+  using Cfg = PrefillCfg<D>;
+  const int tiles = (n + Cfg::BR - 1) / Cfg::BR;
+  const long long blocks = (long long)tiles * hq * batch;
+  prefill_fwd_kernel<T, D, CAUSAL><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
+      static_cast<const char*>(q), static_cast<const char*>(k), static_cast<const char*>(v), static_cast<char*>(o),
+      batch, hq, hkv, n, scale * kLog2e, tiles);
+  return hipGetLastError();
+}
+
+template <class T, int D>
+static hipError_t launch_prefill_d(const void* q, const void* k, const void* v, void* o, int batch, int hq, int hkv,
+                                   int n, float scale, bool causal, hipStream_t stream) {
+  return causal ? launch_prefill_t<T, D, true>(q, k, v, o, batch, hq, hkv, n, scale, stream)
+                : launch_prefill_t<T, D, false>(q, k, v, o, batch, hq, hkv, n, scale, stream);
+}
+
+hipError_t launch_prefill(const void* q, const void* k, const void* v, void* o, bool bf16, int batch, int hq,
+                          int hkv, int n, int d, float scale, bool causal, hipStream_t stream) {
+  if (bf16)
+    return d == 64 ? launch_prefill_d<Bf16, 64>(q, k, v, o, batch, hq, hkv, n, scale, causal, stream)
+                   : launch_prefill_d<Bf16, 128>(q, k, v, o, batch, hq, hkv, n, scale, causal, stream);
+  return d == 64 ? launch_prefill_d<F16, 64>(q, k, v, o, batch, hq, hkv, n, scale, causal, stream)
+                 : launch_prefill_d<F16, 128>(q, k, v, o, batch, hq, hkv, n, scale, causal, stream);
+}
+
+}  // namespace attn

@@ -1,0 +1,155 @@
+/*
+ * attn.h -- C ABI of libattn.so: exact softmax attention on MI355X (gfx950).
+ *
+ * The library computes O = softmax(Q·Kᵀ·scale)·V exactly, tile by tile, with
+ * the online-softmax recurrence: a running maximum m, running sum l and
+ * unnormalised output o per query row, rescaled by exp(m − m_new) whenever a
+ * new key tile raises the maximum, and O = o / l at the end.  The score matrix
+ * never reaches device memory.  Definitions: the three-line math block and
+ * "The online softmax" of "Attention from the kernel's side: FlashAttention,
+ * online softmax and fused dequant"; "Concept" and "Maths" of "Attention
+ * kernels".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor pointer is a device pointer, owned and allocated by the
+ *   caller; every tensor is dense and row-major with the head dimension
+ *   innermost.  The library never allocates or frees device memory and never
+ *   synchronises.
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Each
+ *   call only enqueues kernels on it and returns.  ATTN_OK means the launches
+ *   were accepted; faults during execution surface at the caller's next
+ *   synchronisation.
+ * - All argument checks happen on the host before anything is launched; a
+ *   failed check launches nothing and returns its status.  There is no silent
+ *   fallback to another algorithm.
+ * - Element types: ATTN_BF16 or ATTN_F16 storage; products are accumulated in
+ *   fp32 and the softmax state is kept in fp32.  Outputs are rounded to the
+ *   output type with round-to-nearest-even.
+ * - Supported head dimensions: d = 64 and d = 128.
+ * - Grouped-query attention: query head h reads KV head h / (hq / hkv)
+ *   ("GQA in the kernel", section 5 of "Attention Computation in Practice");
+ *   hq must be a multiple of hkv.
+ * - Every tensor pointer must be 16-byte aligned (the kernels use 128-bit
+ *   loads and stores).
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL_PTR = 1,    /* a required pointer is NULL */
+  ATTN_ERR_BAD_SHAPE = 2,   /* a size is < 1, hq % hkv != 0, or scale is not finite */
+  ATTN_ERR_UNSUPPORTED = 3, /* d not in {64, 128}, or an unknown element type */
+  ATTN_ERR_MISALIGNED = 4,  /* a tensor pointer is not 16-byte aligned */
+  ATTN_ERR_LAUNCH = 5,      /* the HIP runtime rejected a kernel launch */
+  ATTN_ERR_TOO_LARGE = 6    /* a size exceeds what the kernels index (see each call) */
+} attn_status;
+
+typedef enum { ATTN_F16 = 0, ATTN_BF16 = 1 } attn_dtype;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* attn_status_string(int status);
+
+/*
+ * attn_prefill_fwd -- prefill forward over a square problem.
+ *
+ * Computes, for every batch b, query head h and query row i,
+ *   O[b,h,i,:] = sum_j softmax_j(scale · Q[b,h,i,:]·K[b,kh,j,:]) · V[b,kh,j,:],
+ * kh = h / (hq / hkv), over keys j in [0, n) -- or j <= i when `causal` is
+ * non-zero (key j visible to query i iff j <= i: "Masking variants" in
+ * section 5 of "Attention Computation in Practice").  The recurrence runs over
+ * key tiles held in LDS; tiles wholly above the diagonal are skipped, tiles
+ * wholly below it need no mask (the block classification of the same
+ * section).
+ *
+ *   q, o : [batch, hq,  n, d]  elements of `dtype`; o is written, q is read
+ *   k, v : [batch, hkv, n, d]  elements of `dtype`, read only
+ *   scale: the score scale, normally 1/sqrt(d); must be finite
+ *   causal: 0 = every key visible, non-zero = causal mask j <= i
+ *
+ * Limits: batch, hq, hkv, n >= 1; batch·hq·n·d and batch·hkv·n·d below 2^40
+ * elements, n below 2^31 / d (else ATTN_ERR_TOO_LARGE).  O must not alias Q,
+ * K or V.
+ */
+attn_status attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, int dtype, int batch,
+                             int hq, int hkv, int n, int d, float scale, int causal, void* stream);
+
+/*
+ * Split-K ("Flash-Decoding") single-query decode, in two calls: partial states
+ * per key slice, then their merge.  Splitting the cache sequence across
+ * workgroups is what lets one query fill the GPU ("Prefill and decode are
+ * different problems" on the first page; "The four attention kernels you
+ * actually use" in section 5 of "Attention Computation in Practice"; "Concept"
+ * on "Attention kernels").
+ *
+ * Split s of sequence b covers cache rows [s·C, min((s+1)·C, kv_lens[b]))
+ * where C = attn_decode_chunk_len(max_kv_len, num_splits).
+ */
+
+/* A split count that fills the GPU for this shape (host heuristic, >= 1). */
+int attn_decode_num_splits(int batch, int hkv, int max_kv_len);
+
+/* Keys per split C for the given split count (a multiple of 64, >= 64);
+ * returns 0 if max_kv_len < 1 or num_splits < 1. */
+int attn_decode_chunk_len(int max_kv_len, int num_splits);
+
+/* Bytes of partial state the caller must provide: part_m and part_l of
+ * batch·hq·num_splits floats each, part_o of batch·hq·num_splits·d floats.
+ * Returns 0 on a non-positive argument. */
+size_t attn_decode_workspace_bytes(int batch, int hq, int d, int num_splits);
+
+/*
+ * attn_decode_splitk -- partial (m, l, o) of one query per (sequence, head)
+ * over each split of its KV cache.
+ *
+ *   q       : [batch, hq, d]                elements of `dtype`
+ *   k_cache : [batch, hkv, max_kv_len, d]   elements of `dtype`
+ *   v_cache : [batch, hkv, max_kv_len, d]   elements of `dtype`
+ *   kv_lens : [batch] int32, DEVICE memory; sequence b sees cache rows
+ *             0 .. kv_lens[b]-1.  Precondition 0 <= kv_lens[b] <= max_kv_len;
+ *             the kernel clamps each length into that range, and never reads
+ *             a cache row at or past it.
+ *   part_m, part_l : [batch, hq, num_splits] fp32, written
+ *   part_o         : [batch, hq, num_splits, d] fp32, written
+ *
+ * Natural-log units: part_m is the largest scaled score (scale·q·k) in the
+ * split, part_l = sum_j exp(s_j − m) and part_o = sum_j exp(s_j − m)·v_j
+ * (unnormalised).  An empty split writes (m, l, o) = (−inf, 0, 0): the state
+ * of a worker that saw no keys ("Maths" and "Code" on "Attention kernels").
+ * Each workgroup reads the K/V tile of its KV head once and uses it for all
+ * hq/hkv query heads that share it.
+ *
+ * Limits: batch, hq, hkv, max_kv_len, num_splits >= 1; batch·hkv·max_kv_len·d
+ * below 2^40; max_kv_len below 2^31 / d (else ATTN_ERR_TOO_LARGE).
+ */
+attn_status attn_decode_splitk(const void* q, const void* k_cache, const void* v_cache, const int* kv_lens,
+                               int max_kv_len, int dtype, int batch, int hq, int hkv, int d, float scale,
+                               int num_splits, float* part_m, float* part_l, float* part_o, void* stream);
+
+/*
+ * attn_merge_partials -- merge the partial states of each (sequence, head)
+ * and normalise: m = max_s m_s, l = sum_s l_s·exp(m_s − m),
+ * o = sum_s o_s·exp(m_s − m), O = o / l (the two-state merge rule of "Maths"
+ * on "Attention kernels", applied across all splits).  A partial with
+ * m_s = −inf contributes nothing; if every partial is empty (l = 0) the
+ * output row is 0.
+ *
+ *   part_m, part_l : [batch, hq, num_splits] fp32, read
+ *   part_o         : [batch, hq, num_splits, d] fp32, read
+ *   o              : [batch, hq, d] elements of `out_dtype`, written
+ */
+attn_status attn_merge_partials(const float* part_m, const float* part_l, const float* part_o, int batch,
+                                int hq, int d, int num_splits, void* o, int out_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */

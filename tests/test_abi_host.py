@@ -1,0 +1,126 @@
+"""The C ABI on the host (CPU only): the library loads, exports every function
+include/attn.h declares, and rejects bad arguments before launching anything.
+
+Every call here fails validation (or is a pure host helper), so no kernel is
+ever launched and no device is touched.
+"""
+
+import ctypes
+import os
+
+import pytest
+
+from exact_attention_flashattention_amd import _lib
+
+OK, NULL, SHAPE, UNSUP, MISAL, LAUNCH, BIG = range(7)
+BF16, F16 = _lib.ATTN_BF16, _lib.ATTN_F16
+P = 0x10000  # an aligned, non-null stand-in pointer (never dereferenced: every call below fails validation)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_library_exports_every_declared_function(lib):
+    names = _lib.header_functions()
+    assert set(names) == set(_lib.SIGNATURES), "binding signatures out of sync with include/attn.h"
+    raw = ctypes.CDLL(_lib.LIB_PATH)
+    for name in names:
+        assert hasattr(raw, name), name
+
+
+def test_status_strings(lib):
+    for code in range(7):
+        assert lib.attn_status_string(code)
+    assert lib.attn_status_string(99) == b"unknown status"
+
+
+def prefill(lib, q=P, k=P, v=P, o=P, dtype=BF16, batch=1, hq=2, hkv=1, n=16, d=64, scale=0.125, causal=0):
+    return lib.attn_prefill_fwd(q, k, v, o, dtype, batch, hq, hkv, n, d, scale, causal, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), NULL), (dict(k=None), NULL), (dict(v=None), NULL), (dict(o=None), NULL),
+    (dict(batch=0), SHAPE), (dict(hq=0), SHAPE), (dict(hkv=0), SHAPE), (dict(n=0), SHAPE), (dict(n=-5), SHAPE),
+    (dict(hq=3, hkv=2), SHAPE), (dict(scale=float("nan")), SHAPE), (dict(scale=float("inf")), SHAPE),
+    (dict(scale=0.0), SHAPE), (dict(scale=-0.1), SHAPE),
+    (dict(d=96), UNSUP), (dict(d=256), UNSUP), (dict(d=32), UNSUP), (dict(dtype=7), UNSUP),
+    (dict(q=P + 8), MISAL), (dict(k=P + 2), MISAL), (dict(v=P + 4), MISAL), (dict(o=P + 1), MISAL),
+    (dict(batch=1 << 20, hq=1 << 10, hkv=1 << 10, n=1 << 10, d=128), BIG),
+    (dict(n=1 << 25, d=128), BIG),
+])
+def test_prefill_rejects_bad_arguments(lib, kw, status):
+    assert prefill(lib, **kw) == status
+
+
+def decode(lib, q=P, kc=P, vc=P, lens=P, L=100, dtype=BF16, batch=1, hq=4, hkv=2, d=128, scale=0.1, S=2,
+           pm=P, pl=P, po=P):
+    return lib.attn_decode_splitk(q, kc, vc, lens, L, dtype, batch, hq, hkv, d, scale, S, pm, pl, po, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), NULL), (dict(kc=None), NULL), (dict(vc=None), NULL), (dict(lens=None), NULL),
+    (dict(pm=None), NULL), (dict(pl=None), NULL), (dict(po=None), NULL),
+    (dict(L=0), SHAPE), (dict(S=0), SHAPE), (dict(batch=0), SHAPE), (dict(hq=3), SHAPE),
+    (dict(scale=float("nan")), SHAPE), (dict(d=80), UNSUP), (dict(dtype=-1), UNSUP),
+    (dict(q=P + 2), MISAL), (dict(kc=P + 8), MISAL), (dict(po=P + 4), MISAL),
+    (dict(batch=70000), BIG), (dict(S=70000), BIG), (dict(L=1 << 25), BIG),
+])
+def test_decode_rejects_bad_arguments(lib, kw, status):
+    assert decode(lib, **kw) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, P, P, 1, 2, 64, 3, P, BF16), NULL), ((P, P, P, 0, 2, 64, 3, P, BF16), SHAPE),
+    ((P, P, P, 1, 2, 64, 0, P, BF16), SHAPE), ((P, P, P, 1, 2, 72, 3, P, BF16), UNSUP),
+    ((P, P, P, 1, 2, 64, 3, P, 5), UNSUP), ((P, P, P + 4, 1, 2, 64, 3, P, BF16), MISAL),
+    ((P, P, P, 1, 2, 64, 3, P + 2, BF16), MISAL),
+])
+def test_merge_rejects_bad_arguments(lib, args, status):
+    assert lib.attn_merge_partials(*args, None) == status
+
+
+def test_decode_split_plan(lib):
+    # one sequence, 8 KV heads, 262144 keys: enough splits to give every CU several waves
+    s = lib.attn_decode_num_splits(1, 8, 262144)
+    assert 8 * s >= 2048
+    c = lib.attn_decode_chunk_len(262144, s)
+    assert c % 64 == 0 and c * s >= 262144 and c * (s - 1) < 262144
+    # many sequences already fill the GPU: few splits; never more splits than useful
+    assert lib.attn_decode_num_splits(64, 8, 32768) <= 8
+    assert lib.attn_decode_num_splits(1, 1, 10) == 1
+    assert lib.attn_decode_num_splits(0, 8, 10) == 1
+    for L in (1, 63, 64, 65, 1000, 262144):
+        for S in (1, 2, 7, 100):
+            c = lib.attn_decode_chunk_len(L, S)
+            assert c >= 64 and c % 64 == 0 and c * S >= L
+    assert lib.attn_decode_chunk_len(0, 3) == 0 and lib.attn_decode_chunk_len(5, 0) == 0
+
+
+def test_decode_workspace_bytes(lib):
+    assert lib.attn_decode_workspace_bytes(2, 32, 128, 7) == 2 * 32 * 7 * 130 * 4
+    assert lib.attn_decode_workspace_bytes(0, 32, 128, 7) == 0
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    saved = _lib._LIB
+    _lib._LIB = None
+    try:
+        with pytest.raises(ImportError):
+            _lib.load(str(tmp_path / "missing.so"))
+    finally:
+        _lib._LIB = saved
+
+
+def test_no_cpu_fallback_in_binding():
+    """The binding holds no attention arithmetic of its own: it never imports the
+    oracle and never calls a torch attention routine."""
+    pkg = os.path.dirname(_lib.__file__)
+    for fn in os.listdir(pkg):
+        if fn.endswith(".py"):
+            src = open(os.path.join(pkg, fn)).read()
+            assert "oracle" not in src.replace("no oracle", "")
+            assert "scaled_dot_product_attention" not in src
+            for call in ("softmax(", ".exp(", "matmul", "bmm(", "einsum"):
+                assert call not in src, (fn, call)

@@ -1,0 +1,267 @@
+"""GPU parity: the HIP kernels, called through the C ABI, against the fp64 oracle.
+
+Tolerance (written here, applied to every output element): with
+Δ = float64(GPU output) − oracle (fp64, unrounded, on the same rounded
+inputs), max|Δ| <= 2e-2 and mean|Δ| <= 2e-3.  Partial states (fp32) are held
+to tighter bounds derived from fp32 arithmetic, stated at each check.
+
+Cases run at sizes the oracle finishes in seconds that still span several tiles
+and a ragged tail, plus every benchmarked workload at full size in the launch
+configuration the bench uses, checked on sampled rows (computed one by one by
+the oracle) and on properties that hold at any size.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+MAX_TOL, MEAN_TOL = 2e-2, 2e-3
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def A():
+    import exact_attention_flashattention_amd as A
+    A._lib.load()  # fails loudly if the HIP library is not built
+    return A
+
+
+def f64(t):
+    return t.detach().float().cpu().double().numpy()
+
+
+def assert_close(got, ref, tag):
+    g = f64(got) if isinstance(got, torch.Tensor) else got
+    assert np.all(np.isfinite(g)), f"{tag}: non-finite output"
+    d = np.abs(g - ref)
+    print(f"{tag}: max|d|={d.max():.3e} mean|d|={d.mean():.3e}", flush=True)
+    assert d.max() <= MAX_TOL and d.mean() <= MEAN_TOL, tag
+
+
+def announce(msg):
+    print(f"[gpu case] {msg}", flush=True)
+
+
+# --- prefill ---------------------------------------------------------------------------
+
+def run_prefill_case(A, B, hq, hkv, n, d, causal, dtype, seed):
+    w = workloads.Prefill(f"prefill_case_{B}_{hq}_{hkv}_{n}_{d}_{int(causal)}_{dtype}", B, hq, hkv, n, d, causal, dtype)
+    announce(w.name)
+    q, k, v = (t.to(DEV) for t in workloads.prefill_inputs(w, salt=seed))
+    out = A.prefill_fwd(q, k, v, causal=causal, scale=w.scale)
+    torch.cuda.synchronize()
+    ref = oracle.attention(f64(q), f64(k), f64(v), w.scale, causal)
+    assert_close(out, ref, w.name)
+    return q, k, v, out
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n", [1, 7, 64, 129, 1000])
+def test_prefill_edge_lengths(A, n, d, causal, dtype):
+    run_prefill_case(A, 1, 2, 1, n, d, causal, dtype, seed=n)
+
+
+@pytest.mark.parametrize("hq,hkv", [(1, 1), (4, 4), (8, 2), (8, 1)])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_prefill_heads_and_gqa(A, hq, hkv, d, causal):
+    run_prefill_case(A, 2, hq, hkv, 300, d, causal, "bf16", seed=hq * 10 + hkv)
+
+
+def test_prefill_causal_1head_512_fp16_full(A):
+    """The one-head causal fp16 workload (N=512, d=64), whole output."""
+    w = workloads.WORKLOADS["prefill_causal_b1_h1_n512_d64_f16"]
+    announce(w.name)
+    q, k, v = (t.to(DEV) for t in workloads.prefill_inputs(w))
+    out = A.prefill_fwd(q, k, v, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    assert_close(out, oracle.attention(f64(q), f64(k), f64(v), w.scale, True), w.name)
+    # row 0 sees only key 0: its output is V row 0 exactly
+    assert torch.equal(out[0, 0, 0], v[0, 0, 0])
+
+
+@pytest.mark.parametrize("name", ["prefill_b4_h32_n4096_d64_bf16", "prefill_b4_h32_n4096_d128_bf16",
+                                  "prefill_causal_gqa_b1_hq32_hkv8_n32768_d128_bf16"])
+def test_prefill_full_size_sampled_rows(A, name):
+    """Full-size workloads in the benchmarked launch; sampled rows vs the oracle."""
+    w = workloads.WORKLOADS[name]
+    announce(w.name)
+    q, k, v = workloads.prefill_inputs(w, device=DEV)
+    out = A.prefill_fwd(q, k, v, causal=w.causal, scale=w.scale)
+    out2 = A.prefill_fwd(q, k, v, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2), "prefill is not deterministic"
+    assert not torch.isnan(out).any()
+    rng = np.random.default_rng(7)
+    g = w.hq // w.hkv
+    heads = sorted({0, w.hq - 1, *rng.integers(0, w.hq, 2).tolist()})
+    for b in sorted({0, w.batch - 1}):
+        for h in heads:
+            rows = np.unique(np.concatenate([np.arange(0, 130), np.arange(w.n - 130, w.n),
+                                             np.arange(127, w.n, 1024), rng.integers(0, w.n, 64)]))
+            K, V = f64(k[b, h // g]), f64(v[b, h // g])
+            ref = oracle.attention_rows(f64(q[b, h, rows]), K, V, w.scale, rows if w.causal else None)
+            assert_close(out[b, h, rows], ref, f"{w.name} b={b} h={h}")
+
+
+# --- decode ----------------------------------------------------------------------------
+
+def decode_case(A, w, kv_lens, max_len, batch, num_splits, check_partials=True, seed=0):
+    announce(f"{w.name} B={batch} L={max_len} lens={kv_lens.tolist()[:6]} S={num_splits}")
+    q, kc, vc, lens = workloads.decode_inputs(w, device=DEV, salt=seed, kv_lens=kv_lens, max_kv_len=max_len,
+                                              batch=batch)
+    lens_d = lens.to(DEV)
+    S = A.decode_num_splits(batch, w.hkv, max_len) if num_splits is None else num_splits
+    pm, pl, po = A.decode_splitk(q, kc, vc, lens_d, S, w.scale)
+    out = A.merge_partials(pm, pl, po, q.dtype)
+    torch.cuda.synchronize()
+    qf, kf, vf = f64(q), f64(kc), f64(vc)
+    ref = oracle.decode(qf, kf, vf, lens.numpy(), w.scale)
+    assert_close(out, ref, f"{w.name} S={S}")
+    if check_partials:
+        C = A.decode_chunk_len(max_len, S)
+        g = w.hq // w.hkv
+        pm_, pl_, po_ = f64(pm), f64(pl), f64(po)
+        for b in range(batch):
+            for h in range(w.hq):
+                for s in range(S):
+                    j0, j1 = s * C, min((s + 1) * C, int(lens[b]))
+                    if j1 <= j0:
+                        assert pm_[b, h, s] == -np.inf and pl_[b, h, s] == 0.0 and not po_[b, h, s].any()
+                        continue
+                    m, l, o = oracle.split_partials(qf[b, h], kf[b, h // g, j0:j1], vf[b, h // g, j0:j1], w.scale,
+                                                    1)[0]
+                    # fp32 scores and exp2 with the scale folded in: m to 1e-4·(1+|m|); l rescaled to the
+                    # oracle's m to 1e-4 relative; o/l to the output tolerance
+                    assert abs(pm_[b, h, s] - m) <= 1e-4 * (1 + abs(m)), (b, h, s)
+                    l_adj = pl_[b, h, s] * math.exp(pm_[b, h, s] - m)
+                    assert abs(l_adj - l) <= 1e-4 * l, (b, h, s)
+                    assert np.max(np.abs(po_[b, h, s] / pl_[b, h, s] - o / l)) <= MAX_TOL, (b, h, s)
+    return q, kc, vc, lens, out
+
+
+DEC = workloads.WORKLOADS["decode_b1_hq32_hkv8_d128_len262144_bf16"]
+RAG = workloads.WORKLOADS["decode_ragged_b64_hq64_hkv8_d128_len1024to32768_q8_bf16"]
+
+
+@pytest.mark.parametrize("S", [1, None, 7, 200])
+def test_decode_split_counts(A, S):
+    """Split counts 1, the heuristic's, 7, and more splits than 64-key chunks (empty splits)."""
+    decode_case(A, DEC, torch.tensor([5000], dtype=torch.int32), 5000, 1, S)
+
+
+@pytest.mark.parametrize("S", [1, 4])
+def test_decode_lengths_around_chunk_edges(A, S):
+    """Lengths 1, 2, C-1, C, C+1, 2C+1 and Lmax-1, Lmax around the split size C."""
+    Lmax = 1024
+    C = A.decode_chunk_len(Lmax, S)
+    Ls = sorted({1, 2, C - 1, C, min(C + 1, Lmax), min(2 * C + 1, Lmax), Lmax - 1, Lmax})
+    lens = torch.tensor(Ls, dtype=torch.int32)
+    decode_case(A, DEC, lens, Lmax, len(Ls), S)
+
+
+def test_decode_clamps_out_of_range_lengths(A):
+    """A length past the cache is read as the cache length, a negative one as 0."""
+    w = DEC
+    announce("decode clamp")
+    q, kc, vc, _ = workloads.decode_inputs(w, device=DEV, max_kv_len=300, batch=2)
+    bad = torch.tensor([305, -3], dtype=torch.int32, device=DEV)
+    out = A.decode(q, kc, vc, bad, 3, w.scale)
+    torch.cuda.synchronize()
+    ref = oracle.decode(f64(q), f64(kc), f64(vc), [300, 0], w.scale)
+    assert_close(out, ref, "decode clamp")
+
+
+def test_decode_single_key_is_exact(A):
+    q, kc, vc, lens, out = decode_case(A, DEC, torch.tensor([1, 1], dtype=torch.int32), 64, 2, 3)
+    g = DEC.hq // DEC.hkv
+    for h in range(DEC.hq):
+        assert torch.equal(out[:, h], vc[:, h // g, 0]), h
+
+
+def test_decode_zero_length_gives_zero(A):
+    q, kc, vc, lens, out = decode_case(A, DEC, torch.tensor([0, 300], dtype=torch.int32), 512, 2, 4)
+    assert not out[0].float().abs().sum().item()
+
+
+@pytest.mark.parametrize("hq,hkv,d,dtype", [(4, 4, 128, "bf16"), (16, 1, 64, "bf16"), (24, 1, 128, "f16"),
+                                            (32, 2, 64, "f16"), (8, 8, 64, "bf16")])
+def test_decode_head_layouts(A, hq, hkv, d, dtype):
+    """MHA (g=1), g=16, g=24 (two query groups per KV head), fp16 and d=64."""
+    w = workloads.Decode(f"decode_case_{hq}_{hkv}_{d}_{dtype}", 3, hq, hkv, d, 700, None, 1.0, dtype)
+    decode_case(A, w, torch.tensor([700, 333, 64], dtype=torch.int32), 700, 3, 5)
+
+
+def test_decode_ragged_reduced(A):
+    lens = torch.tensor([1024, 3000, 1500, 4096], dtype=torch.int32)
+    decode_case(A, RAG, lens, 4096, 4, None)
+
+
+def test_decode_long_context_full(A):
+    """One sequence over a 262144-key cache, the benchmarked launch, whole output."""
+    announce(DEC.name)
+    q, kc, vc, lens = workloads.decode_inputs(DEC, device=DEV)
+    out = A.decode(q, kc, vc, lens.to(DEV), None, DEC.scale)
+    out2 = A.decode(q, kc, vc, lens.to(DEV), None, DEC.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    g = DEC.hq // DEC.hkv
+    qf = f64(q)
+    ref = np.zeros((1, DEC.hq, DEC.d))
+    for kh in range(DEC.hkv):
+        K, V = f64(kc[0, kh]), f64(vc[0, kh])
+        ref[0, kh * g:(kh + 1) * g] = oracle.attention_rows(qf[0, kh * g:(kh + 1) * g], K, V, DEC.scale)
+    assert_close(out, ref, DEC.name)
+
+
+def test_decode_ragged_full_sampled(A):
+    """64 ragged sequences (lengths 1024..32768, q x8): the benchmarked launch;
+    8 sequences (shortest, longest and 6 random) checked whole against the oracle."""
+    announce(RAG.name)
+    q, kc, vc, lens = workloads.decode_inputs(RAG, device=DEV)
+    out = A.decode(q, kc, vc, lens.to(DEV), None, RAG.scale)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any()
+    g = RAG.hq // RAG.hkv
+    rng = np.random.default_rng(3)
+    Ls = lens.numpy()
+    seqs = sorted({int(Ls.argmin()), int(Ls.argmax()), *rng.integers(0, RAG.batch, 6).tolist()})
+    for b in seqs:
+        L = int(Ls[b])
+        ref = np.zeros((RAG.hq, RAG.d))
+        for kh in range(RAG.hkv):
+            K, V = f64(kc[b, kh, :L]), f64(vc[b, kh, :L])
+            ref[kh * g:(kh + 1) * g] = oracle.attention_rows(f64(q[b, kh * g:(kh + 1) * g]), K, V, RAG.scale)
+        assert_close(out[b], ref, f"{RAG.name} b={b} L={L}")
+
+
+# --- merge -----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("S", [1, 2, 9, 300])
+@pytest.mark.parametrize("d,dtype", [(128, torch.bfloat16), (64, torch.float16)])
+def test_merge_random_partials(A, S, d, dtype):
+    announce(f"merge S={S} d={d} {dtype}")
+    gen = torch.Generator().manual_seed(S * 1000 + d)
+    B, H = 3, 5
+    m = torch.rand(B, H, S, generator=gen) * 40 - 5
+    l = torch.rand(B, H, S, generator=gen) * 50 + 1
+    o = torch.randn(B, H, S, d, generator=gen) * l[..., None]
+    empty = torch.rand(B, H, S, generator=gen) < 0.3
+    empty[0, 0] = True  # one row with no keys at all
+    m[empty] = -math.inf
+    l[empty] = 0
+    o[empty] = 0
+    out = A.merge_partials(m.to(DEV), l.to(DEV), o.to(DEV), dtype)
+    torch.cuda.synchronize()
+    ref = oracle.merge_partials(m.double().numpy(), l.double().numpy(), o.double().numpy())
+    assert_close(out, ref, f"merge S={S} d={d}")
+    assert not out[0, 0].float().abs().sum().item()
