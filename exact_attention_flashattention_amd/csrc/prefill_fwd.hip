@@ -34,6 +34,9 @@ namespace attn {
 
 namespace {
 
+// Largest growth of a row maximum (in log2 units) absorbed without rescaling.
+constexpr float kRescaleLog2 = 8.f;
+
 template <int D>
 struct PrefillCfg {
   static constexpr int WAVES = 4;
@@ -52,7 +55,7 @@ struct PrefillCfg {
 }  // namespace
 
 template <class T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void prefill_fwd_kernel(const char* __restrict__ q, const char* __restrict__ k,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_fwd_kernel(const char* __restrict__ q, const char* __restrict__ k,
                                                           const char* __restrict__ v, char* __restrict__ o, int batch,
                                                           int hq, int hkv, int n, float c, int num_q_tiles) {
   using Cfg = PrefillCfg<D>;
@@ -65,13 +68,30 @@ __global__ __launch_bounds__(256) void prefill_fwd_kernel(const char* __restrict
   const int wave = tid >> 6;
   const int half = lane >> 5;
 
-  // work item: query heads vary fastest, then batch, then query tile
-  int id = blockIdx.x;
-  const int h = id % hq;
-  id /= hq;
-  const int b = id % batch;
-  const int t = id / batch;
-  const int qt = CAUSAL ? (num_q_tiles - 1 - t) : t;  // causal: longest rows first
+  // Work item.  Workgroups are dealt round-robin to the 8 XCDs (blockIdx % 8),
+  // each with its own L2; when the (batch, head) count divides by 8, XCD x is
+  // given the heads [x·H/8, (x+1)·H/8) so the K/V it streams stay in its L2.
+  // Non-causal: an XCD walks its heads one at a time, all query tiles of a
+  // head back to back.  Causal: an XCD interleaves its heads and walks query
+  // tiles longest-first, which balances the triangular work.
+  const int H = batch * hq;
+  int bh, qt;
+  if (H % 8 == 0) {
+    const int per = H / 8;
+    const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+    if (CAUSAL) {
+      bh = xcd * per + slot % per;
+      qt = num_q_tiles - 1 - slot / per;
+    } else {
+      bh = xcd * per + slot / num_q_tiles;
+      qt = slot % num_q_tiles;
+    }
+  } else {
+    bh = blockIdx.x % H;
+    qt = CAUSAL ? num_q_tiles - 1 - (int)(blockIdx.x / H) : (int)(blockIdx.x / H);
+  }
+  const int h = bh % hq;
+  const int b = bh / hq;
   const int kvh = h / (hq / hkv);
 
   const int q0 = qt * Cfg::BR;
@@ -162,11 +182,22 @@ __global__ __launch_bounds__(256) void prefill_fwd_kernel(const char* __restrict
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[sb][e]);
-      mx = max_xor32(mx);
-      const float m_new = fmaxf(m_run, mx * c);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;  // a row with no live key yet stays empty
-      const float alpha = fast_exp2(m_run - m_use);          // 0 while m_run = -inf
+        for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s[sb][e], s[sb][e + 1]));
+      const float m_tile = max_xor32(mx) * c;  // the tile's row max, exp2 domain
+      // The reference maximum m_run is raised only when some row's tile max
+      // exceeds it by more than kRescaleLog2 (then l and o are rescaled by
+      // exp2(m_run - m_new), 0 on the first live tile).  Otherwise the stale
+      // maximum is kept: every p stays <= 2^kRescaleLog2, and o/l is unchanged
+      // because o and l share the reference.  The test is wave-uniform.
+      if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleLog2) != 0) {
+        const float m_new = fmaxf(m_run, m_tile);
+        const float alpha = fast_exp2(m_run - (m_new == kNegInf ? 0.f : m_new));
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = (m_run == kNegInf) ? 0.f : m_run;  // a row with no live key yet stays empty
       float psum = 0.f;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
@@ -176,10 +207,7 @@ __global__ __launch_bounds__(256) void prefill_fwd_kernel(const char* __restrict
           s[sb][e] = p;
           psum += p;
         }
-      l_run = fmaf(l_run, alpha, psum);
-      m_run = m_new;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+      l_run += psum;
 
       // P as the B operand of Oᵀ += Vᵀ·Pᵀ, one 16-key k-step per (subtile, ks)
       u32x4 pf[2][2];
