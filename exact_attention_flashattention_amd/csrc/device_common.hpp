@@ -33,6 +33,11 @@ struct Bf16 {
     bf16x2 v = {(__bf16)a, (__bf16)b};  // v_cvt_pk_bf16_f32: round to nearest even
     return __builtin_bit_cast(uint32_t, v);
   }
+  // acc + lo + hi of a packed pair (v_dot2_f32_bf16 against (1, 1))
+  static __device__ __forceinline__ float add_pair(float acc, uint32_t pair) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
+  }
   static __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
                                                    c, 0, 0, 0);
@@ -47,6 +52,10 @@ struct F16 {
   static __device__ __forceinline__ uint32_t pack2(float a, float b) {
     f16x2 v = {(_Float16)a, (_Float16)b};  // v_cvt_f16_f32: round to nearest even
     return __builtin_bit_cast(uint32_t, v);
+  }
+  static __device__ __forceinline__ float add_pair(float acc, uint32_t pair) {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), one, acc, false);
   }
   static __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
@@ -64,6 +73,19 @@ __device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
 __device__ __forceinline__ u32x4 gload16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void gstore16(void* p, u32x4 x) { *reinterpret_cast<u32x4*>(p) = x; }
 __device__ __forceinline__ void gstore8(void* p, u32x2 x) { *reinterpret_cast<u32x2*>(p) = x; }
+
+// Buffer resource over [base, base + bytes): raw buffer loads through it read
+// 0 for any offset at or past `bytes`, so tails need no branches and nothing
+// past the range is ever touched.  The resource lives in scalar registers and
+// must be wave-uniform.
+typedef __amdgpu_buffer_rsrc_t bufres;
+constexpr int kBufferFlags = 0x00020000;  // gfx9 buffer descriptor word 3: 32-bit data format
+__device__ __forceinline__ bufres make_bufres(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferFlags);
+}
+__device__ __forceinline__ u32x4 bload16(bufres r, uint32_t voffset) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voffset, 0, 0));
+}
 
 // LDS access at a byte offset from an LDS base pointer.
 __device__ __forceinline__ u32x4 lds_read16(const char* base, uint32_t off) {

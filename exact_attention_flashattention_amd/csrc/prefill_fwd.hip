@@ -7,24 +7,31 @@
 // (m, l, o) of every row with the online-softmax recurrence, and O is written
 // once.  Scores and probabilities exist only in registers.
 //
-// gfx950 mapping (one workgroup = 4 wavefronts = 128 query rows):
+// gfx950 mapping (one workgroup = 4 wavefronts = 128 query rows, two
+// workgroups per CU so each SIMD runs two waves):
 //   * each wave owns 32 query rows; its Q rows sit in registers as the
 //     B operand of the 32x32x16 matrix instruction;
-//   * K and V tiles of 64 keys are loaded with coalesced 16-byte global loads
-//     into registers one iteration ahead, then stored to a double-buffered
-//     LDS stage, so HBM/L2 latency hides behind the current tile's math;
+//   * K and V tiles of 64 keys are fetched one tile ahead with 16-byte buffer
+//     loads (out-of-range rows read as 0, so the tail needs no branches) and
+//     stored to a double-buffered LDS stage; the loop is unrolled by two so
+//     both stages are addressed with immediate offsets;
 //   * scores are computed transposed, Sᵀ = K·Qᵀ, so that each lane holds 16
 //     keys of ONE query: the row max needs only an in-lane max plus one
 //     exchange between the wave's halves (v_permlane32_swap), the rescale
 //     factor is one scalar per lane, and the probabilities are already in
 //     the register layout of the B operand of Oᵀ += Vᵀ·Pᵀ (no shuffle);
+//   * each 32-key subtile runs scores -> softmax -> P·V on its own, so the
+//     next subtile's score MFMAs have no dependence on this subtile's
+//     softmax and can issue under it;
 //   * V reaches the matrix cores through the LDS transpose read
 //     (ds_read_b64_tr_b16), which delivers 4 consecutive keys of one
 //     head-dimension column per lane;
 //   * the softmax runs in the exp2 domain (scale·log2 e folded into one FMA
-//     per score, v_exp_f32);
+//     per score, v_exp_f32); the running maximum is raised only when a row's
+//     new maximum exceeds it by more than 2^8 (o and l share the reference, so
+//     o/l is unchanged), which keeps the output rescale off the common path;
 //   * causal: key tiles wholly above a wave's diagonal are skipped, the mask
-//     is applied only on tiles that cross the diagonal or the sequence end
+//     is applied only on subtiles that cross the diagonal or the sequence end
 //     (block classification of "Masking variants", "Attention Computation in
 //     Practice" section 5), and the heaviest query tiles are launched first.
 #include "device_common.hpp"
@@ -40,27 +47,29 @@ constexpr float kRescaleLog2 = 8.f;
 template <int D>
 struct PrefillCfg {
   static constexpr int WAVES = 4;
-  static constexpr int BR = 32 * WAVES;       // query rows per workgroup
-  static constexpr int BC = 64;               // keys per tile
-  static constexpr int KP = 2 * D + 16;       // LDS pitch of a K row (bytes): 4-bank row skew
-  static constexpr int VP = 2 * D + 64;       // LDS pitch of a V row (bytes): 16-bank row skew
+  static constexpr int BR = 32 * WAVES;        // query rows per workgroup
+  static constexpr int BC = 64;                // keys per tile
+  static constexpr int KP = 2 * D + 16;        // LDS pitch of a K row (bytes): 4-bank row skew
+  static constexpr int VP = 2 * D + 64;        // LDS pitch of a V row (bytes): 16-bank row skew
   static constexpr int KBYTES = BC * KP;
   static constexpr int VBYTES = BC * VP;
   static constexpr int STAGE = KBYTES + VBYTES;
   static constexpr int LDS = 2 * STAGE;
-  static constexpr int CPR = D / 8;           // 16-byte chunks per row
+  static constexpr int CPR = D / 8;            // 16-byte chunks per row
   static constexpr int LOADS = BC * CPR / 256; // 16-byte chunks per thread per tile, each of K and V
+  static constexpr int ROWS_PER_LOAD = 256 / CPR;
 };
 
 }  // namespace
 
 template <class T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_fwd_kernel(const char* __restrict__ q, const char* __restrict__ k,
-                                                          const char* __restrict__ v, char* __restrict__ o, int batch,
-                                                          int hq, int hkv, int n, float c, int num_q_tiles) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_fwd_kernel(
+    const char* __restrict__ q, const char* __restrict__ k, const char* __restrict__ v, char* __restrict__ o,
+    int batch, int hq, int hkv, int n, float c, int num_q_tiles) {
   using Cfg = PrefillCfg<D>;
   constexpr int KK = D / 16;  // 32x32x16 k-steps over the head dimension
   constexpr int DT = D / 32;  // 32-row output tiles of the head dimension
+  constexpr uint32_t ROWB = 2 * D;
   __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS];
 
   const int tid = threadIdx.x;
@@ -97,15 +106,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int q0 = qt * Cfg::BR;
   const int qw = q0 + wave * 32;
   const int qrow = qw + (lane & 31);
-  const size_t qo_base = ((size_t)b * hq + h) * (size_t)n * D * 2;
-  const size_t kv_base = ((size_t)b * hkv + kvh) * (size_t)n * D * 2;
+  const size_t qo_base = ((size_t)b * hq + h) * (size_t)n * ROWB;
+  const size_t kv_base = ((size_t)b * hkv + kvh) * (size_t)n * ROWB;
   const char* kp = k + kv_base;
   const char* vp = v + kv_base;
 
   // Q operand (B of Sᵀ = K·Qᵀ): lane holds query qrow, head-dim elements kk·16 + 8·half .. +7
   u32x4 qf[KK];
   {
-    const char* qp = q + qo_base + (size_t)qrow * D * 2;
+    const char* qp = q + qo_base + (size_t)qrow * ROWB;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) qf[kk] = qrow < n ? gload16(qp + (kk * 16 + 8 * half) * 2) : zero4();
   }
@@ -114,27 +123,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int nkt = (kend + Cfg::BC - 1) / Cfg::BC;
   const int wave_last = min(n - 1, qw + 31);          // last live query row of this wave
 
+  // Tile loads: thread tid moves chunk (tid % CPR) of rows tid/CPR + i·ROWS_PER_LOAD.
+  const uint32_t g_off = (uint32_t)(tid / Cfg::CPR) * ROWB + (tid % Cfg::CPR) * 16;
+  const uint32_t k_st = (uint32_t)(tid / Cfg::CPR) * Cfg::KP + (tid % Cfg::CPR) * 16;
+  const uint32_t v_st = Cfg::KBYTES + (uint32_t)(tid / Cfg::CPR) * Cfg::VP + (tid % Cfg::CPR) * 16;
   u32x4 kst[Cfg::LOADS], vst[Cfg::LOADS];
   auto load_tile = [&](int it) {
-    const int j0 = it * Cfg::BC;
+    // rows [j0, j0 + BC) of this head, clipped to the sequence: rows past n read as 0
+    const int j0 = min(it * Cfg::BC, n);
+    const uint32_t bytes = (uint32_t)min(Cfg::BC, n - j0) * ROWB;
+    const bufres rk = make_bufres(kp + (size_t)j0 * ROWB, bytes);
+    const bufres rv = make_bufres(vp + (size_t)j0 * ROWB, bytes);
 #pragma unroll
     for (int i = 0; i < Cfg::LOADS; ++i) {
-      const int cidx = tid + 256 * i;
-      const int key = j0 + cidx / Cfg::CPR;
-      const size_t off = (size_t)key * D * 2 + (cidx % Cfg::CPR) * 16;
-      kst[i] = key < n ? gload16(kp + off) : zero4();
-      vst[i] = key < n ? gload16(vp + off) : zero4();
+      kst[i] = bload16(rk, g_off + i * Cfg::ROWS_PER_LOAD * ROWB);
+      vst[i] = bload16(rv, g_off + i * Cfg::ROWS_PER_LOAD * ROWB);
     }
   };
-  auto store_tile = [&](int buf) {
-    char* ks = lds + buf * Cfg::STAGE;
-    char* vs = ks + Cfg::KBYTES;
+  auto store_tile = [&](int stage) {
+    char* base = lds + stage * Cfg::STAGE;
 #pragma unroll
     for (int i = 0; i < Cfg::LOADS; ++i) {
-      const int cidx = tid + 256 * i;
-      const int row = cidx / Cfg::CPR, col = cidx % Cfg::CPR;
-      lds_write16(ks, row * Cfg::KP + col * 16, kst[i]);
-      lds_write16(vs, row * Cfg::VP + col * 16, vst[i]);
+      lds_write16(base, k_st + i * Cfg::ROWS_PER_LOAD * Cfg::KP, kst[i]);
+      lds_write16(base, v_st + i * Cfg::ROWS_PER_LOAD * Cfg::VP, vst[i]);
     }
   };
 
@@ -145,50 +156,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[dt][e] = 0.f;
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  // per-lane LDS bases: K operand row, V transpose-read block
+  const int G = lane >> 4, j = lane & 15;
+  const uint32_t k_rd = (lane & 31) * Cfg::KP + half * 16;
+  const uint32_t v_rd = Cfg::KBYTES + (4 * (G >> 1) + (j >> 2)) * Cfg::VP + (16 * (G & 1) + 4 * (j & 3)) * 2;
 
-  for (int it = 0; it < nkt; ++it) {
-    if (it + 1 < nkt) load_tile(it + 1);
+  auto compute = [&](int stage, int it) {
     const int j0 = it * Cfg::BC;
-    if (!CAUSAL || j0 <= wave_last) {
-      const char* ks = lds + (it & 1) * Cfg::STAGE;
-      const char* vs = ks + Cfg::KBYTES;
+    if (CAUSAL && j0 > wave_last) return;  // the whole tile lies above this wave's diagonal
+    const char* st = lds + stage * Cfg::STAGE;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      const int s0 = j0 + 32 * sb;
+      // Sᵀ subtile: s[e] is key s0 + 8·(e/4) + 4·half + e%4 against query qrow
+      f32x16 s;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[e] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) s = T::mfma32(lds_read16(st, k_rd + sb * 32 * Cfg::KP + kk * 32), qf[kk], s);
 
-      // Sᵀ for two 32-key subtiles: s[sb][e] is key j0 + 32·sb + 8·(e/4) + 4·half + e%4 against query qrow
-      f32x16 s[2];
+      if (s0 + 32 > n || (CAUSAL && s0 + 31 > qw)) {
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s[sb][e] = 0.f;
-        const uint32_t krow = (sb * 32 + (lane & 31)) * Cfg::KP + half * 16;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) s[sb] = T::mfma32(lds_read16(ks, krow + kk * 32), qf[kk], s[sb]);
+        for (int e = 0; e < 16; ++e) {
+          const int key = s0 + 8 * (e >> 2) + 4 * half + (e & 3);
+          if (key >= n || (CAUSAL && key > qrow)) s[e] = kNegInf;
+        }
       }
 
-      const bool need_mask = (j0 + Cfg::BC > n) || (CAUSAL && j0 + Cfg::BC - 1 > qw);
-      if (need_mask) {
+      float mx = fmaxf(s[0], s[1]);
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int key = j0 + sb * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-            if (key >= n || (CAUSAL && key > qrow)) s[sb][e] = kNegInf;
-          }
-      }
-
-      float mx = kNegInf;
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s[sb][e], s[sb][e + 1]));
-      const float m_tile = max_xor32(mx) * c;  // the tile's row max, exp2 domain
-      // The reference maximum m_run is raised only when some row's tile max
-      // exceeds it by more than kRescaleLog2 (then l and o are rescaled by
-      // exp2(m_run - m_new), 0 on the first live tile).  Otherwise the stale
-      // maximum is kept: every p stays <= 2^kRescaleLog2, and o/l is unchanged
-      // because o and l share the reference.  The test is wave-uniform.
+      for (int e = 2; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s[e], s[e + 1]));
+      const float m_tile = max_xor32(mx) * c;  // the subtile's row max, exp2 domain
+      // Raise the reference maximum only when some row's new maximum exceeds it
+      // by more than kRescaleLog2; then l and o are rescaled by
+      // exp2(m_run - m_new) (0 on the first live subtile).  Otherwise every
+      // p stays <= 2^kRescaleLog2.  The test is wave-uniform.
       if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleLog2) != 0) {
         const float m_new = fmaxf(m_run, m_tile);
         const float alpha = fast_exp2(m_run - (m_new == kNegInf ? 0.f : m_new));
@@ -198,52 +200,63 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         m_run = m_new;
       }
       const float m_use = (m_run == kNegInf) ? 0.f : m_run;  // a row with no live key yet stays empty
-      float psum = 0.f;
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float p = fast_exp2(fmaf(s[sb][e], c, -m_use));
-          s[sb][e] = p;
-          psum += p;
-        }
-      l_run += psum;
+      for (int e = 0; e < 16; ++e) s[e] = fast_exp2(fmaf(s[e], c, -m_use));
 
-      // P as the B operand of Oᵀ += Vᵀ·Pᵀ, one 16-key k-step per (subtile, ks)
-      u32x4 pf[2][2];
+      // P, rounded to the storage type, as the B operand of Oᵀ += Vᵀ·Pᵀ (one
+      // 16-key k-step per ks); l adds up exactly these rounded weights.
+      u32x4 pf[2];
+      float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          pf[sb][ks] = u32x4{T::pack2(s[sb][8 * ks + 0], s[sb][8 * ks + 1]), T::pack2(s[sb][8 * ks + 2], s[sb][8 * ks + 3]),
-                             T::pack2(s[sb][8 * ks + 4], s[sb][8 * ks + 5]), T::pack2(s[sb][8 * ks + 6], s[sb][8 * ks + 7])};
+        for (int i = 0; i < 4; ++i) {
+          pf[ks][i] = T::pack2(s[8 * ks + 2 * i], s[8 * ks + 2 * i + 1]);
+          if (i & 1)
+            ps1 = T::add_pair(ps1, pf[ks][i]);
+          else
+            ps0 = T::add_pair(ps0, pf[ks][i]);
+        }
+      l_run += ps0 + ps1;
 
       // V operand (A of Oᵀ += Vᵀ·Pᵀ): lane (group G of 16, index j) takes head-dim column
       // 32·dt + 16·(G&1) + j and keys 32·sb + 16·ks + 4·(G>>1) + {0..3} and the same + 8
-      const int G = lane >> 4, j = lane & 15;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const uint32_t col = (dt * 32 + 16 * (G & 1) + 4 * (j & 3)) * 2;
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            const uint32_t row = sb * 32 + 16 * ks + 4 * (G >> 1) + (j >> 2);
-            const u32x2 va = lds_read_tr16(vs, row * Cfg::VP + col);
-            const u32x2 vb = lds_read_tr16(vs, (row + 8) * Cfg::VP + col);
-            oacc[dt] = T::mfma32(u32x4{va[0], va[1], vb[0], vb[1]}, pf[sb][ks], oacc[dt]);
-          }
-      }
+        for (int ks = 0; ks < 2; ++ks) {
+          const uint32_t off = v_rd + (32 * sb + 16 * ks) * Cfg::VP + dt * 64;
+          const u32x2 va = lds_read_tr16(st, off);
+          const u32x2 vb = lds_read_tr16(st, off + 8 * Cfg::VP);
+          oacc[dt] = T::mfma32(u32x4{va[0], va[1], vb[0], vb[1]}, pf[ks], oacc[dt]);
+        }
     }
-    if (it + 1 < nkt) store_tile((it + 1) & 1);
+  };
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  // Unrolled by two so each LDS stage is addressed with immediates.  The next
+  // tile is always prefetched: past the last tile the loads read 0 (or
+  // in-range rows nobody uses) into a stage that is never read.
+  for (int it = 0;;) {
+    load_tile(it + 1);
+    compute(0, it);
+    store_tile(1);
     __syncthreads();
+    if (++it >= nkt) break;
+    load_tile(it + 1);
+    compute(1, it);
+    store_tile(0);
+    __syncthreads();
+    if (++it >= nkt) break;
   }
 
   // epilogue: O = o / l, rounded to the storage type, written once
   const float l_tot = sum_xor32(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qrow < n) {
-    char* op = o + qo_base + (size_t)qrow * D * 2;
+    char* op = o + qo_base + (size_t)qrow * ROWB;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
