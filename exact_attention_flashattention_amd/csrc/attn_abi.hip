@@ -12,6 +12,7 @@ namespace {
 
 constexpr long long kMaxElems = 1LL << 40;  // per-tensor element bound the kernels' 64-bit offsets assume
 constexpr int kDecodeTargetWaves = 2048;    // decode waves that fill 256 CUs at 8 waves per CU
+constexpr int kDecodeMaxChunk = 1024;       // most keys per split, so ragged lengths balance across waves
 constexpr int kDecodeMinChunk = 256;        // fewest keys worth a split of its own
 constexpr int kChunkAlign = 64;
 
@@ -21,14 +22,20 @@ bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
 
 attn_status from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH; }
 
-// An optional override of the split heuristic for A/B measurements:
-// ATTN_DECODE_TARGET_WAVES=<n> changes the wave count the heuristic aims for.
+// Optional overrides of the split heuristic for A/B measurements:
+// ATTN_DECODE_TARGET_WAVES=<n> (waves to aim for) and ATTN_DECODE_MAX_CHUNK=<n>
+// (most keys per split).  Read once per process.
+int env_int(const char* name, int fallback) {
+  const char* s = std::getenv(name);
+  const long x = s ? std::strtol(s, nullptr, 10) : 0;
+  return (x > 0 && x < (1L << 24)) ? (int)x : fallback;
+}
 int decode_target_waves() {
-  static const int v = [] {
-    const char* s = std::getenv("ATTN_DECODE_TARGET_WAVES");
-    const long x = s ? std::strtol(s, nullptr, 10) : 0;
-    return (x > 0 && x < (1L << 24)) ? (int)x : kDecodeTargetWaves;
-  }();
+  static const int v = env_int("ATTN_DECODE_TARGET_WAVES", kDecodeTargetWaves);
+  return v;
+}
+int decode_max_chunk() {
+  static const int v = env_int("ATTN_DECODE_MAX_CHUNK", kDecodeMaxChunk);
   return v;
 }
 
@@ -62,10 +69,14 @@ attn_status attn_prefill_fwd(const void* q, const void* k, const void* v, void* 
 
 int attn_decode_num_splits(int batch, int hkv, int max_kv_len) {
   if (batch < 1 || hkv < 1 || max_kv_len < 1) return 1;
+  // enough splits to fill the GPU, and enough that no split holds more than
+  // the maximum chunk; never so many that splits drop below the minimum chunk
   const long long heads = (long long)batch * hkv;
-  const long long want = (decode_target_waves() + heads - 1) / heads;
+  const long long fill = (decode_target_waves() + heads - 1) / heads;
+  const long long bound = (max_kv_len + decode_max_chunk() - 1) / decode_max_chunk();
   const long long useful = (max_kv_len + kDecodeMinChunk - 1) / kDecodeMinChunk;
-  long long s = want < useful ? want : useful;
+  long long s = fill > bound ? fill : bound;
+  if (s > useful) s = useful;
   if (s < 1) s = 1;
   if (s > 65535) s = 65535;
   return (int)s;
@@ -108,7 +119,7 @@ attn_status attn_merge_partials(const float* part_m, const float* part_l, const 
   if (!part_m || !part_l || !part_o || !o) return ATTN_ERR_NULL_PTR;
   if (batch < 1 || hq < 1 || num_splits < 1) return ATTN_ERR_BAD_SHAPE;
   if ((d != 64 && d != 128) || !dtype_ok(out_dtype)) return ATTN_ERR_UNSUPPORTED;
-  if ((long long)batch * hq >= (1LL << 31) || (long long)batch * hq * num_splits * d >= kMaxElems)
+  if ((long long)batch * hq * (d / 32) >= (1LL << 31) || (long long)batch * hq * num_splits * d >= kMaxElems)
     return ATTN_ERR_TOO_LARGE;
   if (!aligned16(part_o) || !aligned16(o)) return ATTN_ERR_MISALIGNED;
   return from_hip(attn::launch_merge(part_m, part_l, part_o, batch * hq, d, num_splits, out_dtype == ATTN_BF16, o,

@@ -10,7 +10,8 @@
 // share the KV head, so every K/V byte the wave streams is used by all of
 // them (GQA reuse, "GQA in the kernel").  The wave walks its slice 32 keys at
 // a time; the next 32 keys' K and V rows are already in flight (16-byte
-// global loads into registers) while the current ones are used:
+// buffer loads into registers, clipped to the sequence's length) while the
+// current ones are used:
 //
 //   scores   Sᵀ[32 keys × 16 queries] = K·Qᵀ on 16x16x32 MFMA, K straight
 //            from its registers, Q resident in registers;
@@ -43,12 +44,10 @@ struct DecodeStage {
 }  // namespace
 
 template <class T, int D>
-__global__ __launch_bounds__(64) void decode_splitk_kernel(const char* __restrict__ q, const char* __restrict__ kc,
-                                                           const char* __restrict__ vc,
-                                                           const int* __restrict__ kv_lens, int max_kv_len, int hq,
-                                                           int hkv, int g, int chunk, int num_splits, float c,
-                                                           float* __restrict__ part_m, float* __restrict__ part_l,
-                                                           float* __restrict__ part_o) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void decode_splitk_kernel(
+    const char* __restrict__ q, const char* __restrict__ kc, const char* __restrict__ vc,
+    const int* __restrict__ kv_lens, int max_kv_len, int hq, int hkv, int g, int chunk, int num_splits, float c,
+    float* __restrict__ part_m, float* __restrict__ part_l, float* __restrict__ part_o) {
   constexpr int KK = D / 32;
   constexpr int DT = D / 16;              // 16-row output tiles of the head dimension
   constexpr int VCH = D / 16;
@@ -99,20 +98,29 @@ __global__ __launch_bounds__(64) void decode_splitk_kernel(const char* __restric
   const char* kbase = kc + head_base;
   const char* vbase = vc + head_base;
 
+  // Loads go through buffer resources that cover rows [k0, end) only: rows at
+  // or past the sequence's length read as 0 and are never touched in memory.
+  // The per-lane offsets are fixed; each step only moves the scalar base.
+  uint32_t k_off[2][KK], v_off[VCH];
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) k_off[sb][kk] = (uint32_t)(sb * 16 + r) * D * 2 + (4 * kk + grp) * 16;
+#pragma unroll
+  for (int i = 0; i < VCH; ++i) {
+    const int cidx = lane + 64 * i;
+    v_off[i] = (uint32_t)(cidx / CPR) * D * 2 + (cidx % CPR) * 16;
+  }
   auto load = [&](DecodeStage<D>& st, int k0) {
+    const uint32_t bytes = (uint32_t)(end - k0) * D * 2;
+    const bufres rk = make_bufres(kbase + (size_t)k0 * D * 2, bytes);
+    const bufres rv = make_bufres(vbase + (size_t)k0 * D * 2, bytes);
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      const int key = k0 + sb * 16 + r;
+    for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-        st.k[sb][kk] = key < end ? gload16(kbase + (size_t)key * D * 2 + (4 * kk + grp) * 16) : zero4();
-    }
+      for (int kk = 0; kk < KK; ++kk) st.k[sb][kk] = bload16(rk, k_off[sb][kk]);
 #pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int cidx = lane + 64 * i;
-      const int key = k0 + cidx / CPR;
-      st.v[i] = key < end ? gload16(vbase + (size_t)key * D * 2 + (cidx % CPR) * 16) : zero4();
-    }
+    for (int i = 0; i < VCH; ++i) st.v[i] = bload16(rv, v_off[i]);
   };
 
   float m_run = kNegInf, l_run = 0.f;

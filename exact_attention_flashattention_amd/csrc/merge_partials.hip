@@ -8,80 +8,91 @@
 // m_s = −inf saw no keys and gets weight 0 -- the guard of that page's "Code"
 // section -- and a row with no keys at all is written as 0.
 //
-// One workgroup of 256 threads per (sequence, head).  Each thread owns 4
-// consecutive output columns; the D/4 threads of a column group form one "row
-// group", and the 256/(D/4) row groups take the splits round-robin, so every
-// split's o row is read with contiguous 16-byte loads.  Row-group results are
-// combined through LDS.  Memory-bound: it reads S·(D+2) floats per row once.
+// Launch shape: 256 threads per workgroup; each thread owns 4 consecutive
+// output columns of one split group, and the split groups take the splits
+// round-robin, so every split's o row is read with contiguous 16-byte loads,
+// several in flight per thread.  Each split group folds its splits against
+// its own maximum in registers, then the groups are merged through LDS with
+// the same rule -- one round trip to memory.  A workgroup covers COLS output
+// columns: all D when there are many rows, 32 when few rows would leave most
+// of the GPU idle.  Memory-bound: it reads S·(D+2) floats per row once.
 #include "device_common.hpp"
 #include "launchers.hpp"
 
 namespace attn {
 
-template <class T, int D>
+template <class T, int D, int COLS>
 __global__ __launch_bounds__(256) void merge_partials_kernel(const float* __restrict__ part_m,
                                                              const float* __restrict__ part_l,
                                                              const float* __restrict__ part_o, int num_splits,
                                                              void* __restrict__ out) {
-  constexpr int COLS = D / 4;          // threads per row group
-  constexpr int GROUPS = 256 / COLS;   // row groups
-  __shared__ float red[256];
-  __shared__ f32x4 acc_s[GROUPS][COLS];
-  __shared__ float l_s[GROUPS];
+  constexpr int QUADS = COLS / 4;       // threads per split group
+  constexpr int GROUPS = 256 / QUADS;   // split groups
+  constexpr int CB = D / COLS;          // workgroups per row
+  __shared__ f32x4 acc_s[GROUPS][QUADS];
+  __shared__ float l_s[GROUPS], m_s[GROUPS];
 
   const int tid = threadIdx.x;
-  const size_t row = blockIdx.x;  // b * hq + h
+  const size_t row = blockIdx.x / CB;  // b * hq + h
+  const int col0 = (blockIdx.x % CB) * COLS;
+  const int c = tid % QUADS, g = tid / QUADS;
+  const int col = col0 + 4 * c;
   const float* m_ = part_m + row * num_splits;
   const float* l_ = part_l + row * num_splits;
-  const float* o_ = part_o + row * (size_t)num_splits * D;
+  const float* o_ = part_o + row * (size_t)num_splits * D + col;
 
-  // 1. the largest partial maximum
-  float mx = kNegInf;
-  for (int s = tid; s < num_splits; s += 256) mx = fmaxf(mx, m_[s]);
-  red[tid] = mx;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
-    __syncthreads();
-  }
-  const float M = red[0];
-
-  // 2. weighted sums of o and l over this row group's splits
-  const int c = tid % COLS, g = tid / COLS;
+  // 1. this group's splits against the group's own maximum
+  float mg = kNegInf;
+  for (int s = g; s < num_splits; s += GROUPS) mg = fmaxf(mg, m_[s]);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float lsum = 0.f;
-  if (M != kNegInf) {
+  if (mg != kNegInf) {
+#pragma unroll 4
     for (int s = g; s < num_splits; s += GROUPS) {
       const float ms = m_[s];
-      const float w = (ms == kNegInf) ? 0.f : fast_exp2((ms - M) * kLog2e);
-      const f32x4 os = *reinterpret_cast<const f32x4*>(o_ + (size_t)s * D + 4 * c);
-      acc += w * os;
+      const float w = (ms == kNegInf) ? 0.f : fast_exp2((ms - mg) * kLog2e);
+      acc += w * *reinterpret_cast<const f32x4*>(o_ + (size_t)s * D);
       lsum += w * l_[s];
     }
   }
   acc_s[g][c] = acc;
-  if (c == 0) l_s[g] = lsum;
+  if (c == 0) {
+    l_s[g] = lsum;
+    m_s[g] = mg;
+  }
   __syncthreads();
 
-  // 3. combine row groups and normalise
-  if (tid < COLS) {
-    f32x4 tot = acc_s[0][tid];
-    float l = l_s[0];
-    for (int r = 1; r < GROUPS; ++r) {
-      tot += acc_s[r][tid];
-      l += l_s[r];
+  // 2. merge the groups and normalise (empty groups have m = -inf, weight 0)
+  if (tid < QUADS) {
+    float M = m_s[0];
+    for (int r = 1; r < GROUPS; ++r) M = fmaxf(M, m_s[r]);
+    f32x4 tot = {0.f, 0.f, 0.f, 0.f};
+    float l = 0.f;
+    if (M != kNegInf) {
+      for (int r = 0; r < GROUPS; ++r) {
+        const float w = (m_s[r] == kNegInf) ? 0.f : fast_exp2((m_s[r] - M) * kLog2e);
+        tot += w * acc_s[r][tid];
+        l += w * l_s[r];
+      }
     }
     const float inv = (l > 0.f) ? 1.f / l : 0.f;
     tot *= inv;
     u32x2 packed = {T::pack2(tot[0], tot[1]), T::pack2(tot[2], tot[3])};
-    gstore8(reinterpret_cast<char*>(out) + (row * D + 4 * tid) * 2, packed);
+    gstore8(reinterpret_cast<char*>(out) + (row * D + col0 + 4 * tid) * 2, packed);
   }
 }
+
+// Rows below this count are spread over D/32 workgroups each.
+constexpr int kMergeFewRows = 512;
 
 template <class T, int D>
 static hipError_t launch_merge_t(const float* pm, const float* pl, const float* po, int rows, int num_splits,
                                  void* out, hipStream_t stream) {
-  merge_partials_kernel<T, D><<<dim3(rows), dim3(256), 0, stream>>>(pm, pl, po, num_splits, out);
+  if (rows < kMergeFewRows)
+    merge_partials_kernel<T, D, 32><<<dim3((unsigned)rows * (D / 32)), dim3(256), 0, stream>>>(pm, pl, po,
+                                                                                          num_splits, out);
+  else
+    merge_partials_kernel<T, D, D><<<dim3((unsigned)rows), dim3(256), 0, stream>>>(pm, pl, po, num_splits, out);
   return hipGetLastError();
 }
 
