@@ -87,6 +87,36 @@ __device__ __forceinline__ u32x4 bload16(bufres r, uint32_t voffset) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voffset, 0, 0));
 }
 
+// Buffer-load-to-LDS of 16 bytes per lane: lane i's bytes (from voffset in the
+// buffer described by `rsrc`, 0 past its end) land at LDS byte address
+// `lds_addr + 16·i`.  `lds_addr` must be wave-uniform.
+//
+// Issued as inline assembly on purpose.  The compiler cannot tell which LDS
+// bytes a DMA writes, so after one it makes the next LDS read of ANY address
+// wait for the DMA to finish -- which serialises a prefetch of a later tile
+// with the reads of the current one.  Callers instead wait explicitly
+// (vmcnt(0) and a barrier) before reading the destination; the compiler sees
+// only a memory-clobbering statement and keeps other memory operations in
+// order around it.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 bufres_words(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), (int)bytes, kBufferFlags};
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const ATTN_LDS char*)p;
+}
+__device__ __forceinline__ void dma16_to_lds(i32x4 rsrc, uint32_t voffset, uint32_t lds_byte_addr) {
+  // one wait state between the M0 write and the LDS-DMA that reads it
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voffset),
+      "s"(rsrc), "s"(lds_byte_addr)
+      : "memory");
+}
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
 // LDS access at a byte offset from an LDS base pointer.
 __device__ __forceinline__ u32x4 lds_read16(const char* base, uint32_t off) {
   return *reinterpret_cast<const u32x4*>(base + off);

@@ -105,7 +105,9 @@ prefill_fwd_kernel(const char* __restrict__ q, const char* __restrict__ k, const
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // wave-uniform by construction; readfirstlane lets the compiler keep it (and
+  // the LDS-DMA destinations and buffer resources derived from it) in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
@@ -168,14 +170,16 @@ prefill_fwd_kernel(const char* __restrict__ q, const char* __restrict__ k, const
   auto fetch_tile = [&](int it, int stage) {
     const int j0 = min(it * Cfg::BC, n);
     const int bytes = min(Cfg::BC, n - j0) * (int)ROWB;  // rows past the end read as 0
-    char* st = lds + stage * Cfg::STAGE;
+    const char* kt = kp + (size_t)j0 * ROWB;
+    const char* vt = vp + (size_t)j0 * ROWB;
+    const uint32_t st = lds_addr(lds) + stage * Cfg::STAGE;
 #pragma unroll
     for (int i = 0; i < Cfg::DMA; ++i) {
-      const int off = (i * Cfg::WAVES + wave) * 1024;  // this transfer's first byte in the tile
-      const bufres rk = make_bufres(kp + (size_t)j0 * ROWB + i * Cfg::WAVES * 1024, max(bytes - i * Cfg::WAVES * 1024, 0));
-      const bufres rv = make_bufres(vp + (size_t)j0 * ROWB + i * Cfg::WAVES * 1024, max(bytes - i * Cfg::WAVES * 1024, 0));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (ATTN_LDS void*)(st + off), 16, k_src, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (ATTN_LDS void*)(st + Cfg::TILE + off), 16, v_src, 0, 0, 0);
+      const int first = i * Cfg::WAVES * 1024;          // the transfer group's first byte in the tile
+      const uint32_t off = first + wave * 1024;         // this wave's transfer
+      const int rec = bytes > first ? bytes - first : 0;
+      dma16_to_lds(bufres_words(kt + first, (uint32_t)rec), k_src, st + off);
+      dma16_to_lds(bufres_words(vt + first, (uint32_t)rec), v_src, st + Cfg::TILE + off);
     }
   };
 
@@ -316,10 +320,8 @@ prefill_fwd_kernel(const char* __restrict__ q, const char* __restrict__ k, const
   f32x16 s[NB], s_next[NB];
   u32x4 pf[NB][2];
 
-  auto vm_wait_all = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
-
   fetch_tile(0, 0);
-  vm_wait_all();
+  wait_vm_all();
   __syncthreads();
   if (nkt > 1) fetch_tile(1, 1);
   bool live = !CAUSAL || 0 <= wave_last;
@@ -349,7 +351,7 @@ prefill_fwd_kernel(const char* __restrict__ q, const char* __restrict__ k, const
     if (live1) exp_pack(s_next, pf);
     if (Cfg::STAGES == 2 && live1) pv(pf, stage, 1);
     if (more) {
-      vm_wait_all();   // the next tile has landed (this wave's part)
+      wait_vm_all();   // the next tile has landed (this wave's part)
       __syncthreads(); // ... everyone's part; every wave is past its last read of the stage refilled next
       if (it + 2 < nkt) fetch_tile(it + 2, (stage + 2) % Cfg::STAGES);
       if (live2) qk(s, nstage, 0);
