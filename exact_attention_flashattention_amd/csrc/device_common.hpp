@@ -100,14 +100,21 @@ __device__ __forceinline__ u32x4 bload16(bufres r, uint32_t voffset) {
 // order around it.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ i32x4 bufres_words(const void* base, uint32_t bytes) {
+  // the words must sit in scalar registers even when the compiler computed a
+  // (wave-uniform) input with vector instructions
   const uint64_t a = (uint64_t)(uintptr_t)base;
-  return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), (int)bytes, kBufferFlags};
+  return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+               __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu)),
+               __builtin_amdgcn_readfirstlane((int)bytes), kBufferFlags};
 }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const ATTN_LDS char*)p;
 }
 __device__ __forceinline__ void dma16_to_lds(i32x4 rsrc, uint32_t voffset, uint32_t lds_byte_addr) {
-  // one wait state between the M0 write and the LDS-DMA that reads it
+  // One wait state between the M0 write and the LDS-DMA that reads it.  M0 is
+  // not listed as clobbered (the compiler rejects that for a reserved
+  // register); the compiler itself writes M0 right before any instruction of
+  // its own that reads it, so nothing it holds there lives across this one.
   asm volatile(
       "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"

@@ -7,17 +7,24 @@
 // (m, l, o) of every row with the online-softmax recurrence, and O is written
 // once.  Scores and probabilities exist only in registers.
 //
-// gfx950 mapping.  One workgroup = 4 wavefronts = 256 query rows; each wave
-// owns 64 rows as two 32-row blocks, so every K or V fragment read from LDS
-// feeds two matrix instructions (LDS read bandwidth, not the matrix cores,
-// limits a 32-row-per-wave design on this chip).
+// gfx950 mapping.  One workgroup = 8 wavefronts, two per SIMD, each owning NB
+// blocks of 32 query rows (two at d=64, one at d=128); the K/V tiles in LDS
+// are shared by all eight.
+//   * Two wave groups run anti-phased.  Every wave alternates a matrix step
+//     (score MFMAs of one 32-key subtile, P·V MFMAs of the previous one) and
+//     a vector step (mask, row max, exponentials and packing of a subtile,
+//     plus the LDS reads that feed the next matrix step).  Group 1 runs one
+//     step behind group 0 and every step ends at a workgroup barrier, so on
+//     each SIMD one wave keeps the matrix core busy while its partner does the
+//     softmax arithmetic -- the two units overlap instead of taking turns.
 //   * Q rows sit in registers as the B operand of 32x32x16 MFMA.
 //   * K and V tiles of 64 keys go from HBM/L2 straight into LDS with
-//     buffer-load-to-LDS (no register staging; rows past the sequence end
-//     read as 0).  Three LDS stages: the tile being consumed, the tile whose
-//     last P·V is still in flight, and the tile being fetched -- one barrier
-//     per tile.  Rows are stored unpadded with an XOR swizzle of their 16-byte
-//     chunks, chosen so the K operand reads (ds_read_b128) and the V
+//     buffer-load-to-LDS (rows past the sequence end read as 0), into one of
+//     STAGES buffers; a tile is fetched as soon as both groups are done with
+//     the tile that last used its buffer, and each wave waits for its own
+//     part with an exact vmcnt before the barrier that precedes the tile's
+//     first read.  Rows are stored unpadded with an XOR swizzle of their
+//     16-byte chunks so the K operand reads (ds_read_b128) and the V
 //     transpose reads (ds_read_b64_tr_b16) are free of bank conflicts.
 //   * Scores are computed transposed, Sᵀ = K·Qᵀ, so each lane holds keys of
 //     ONE query: the row max is an in-lane max plus one exchange between the
@@ -28,22 +35,20 @@
 //     Oᵀ += Vᵀ·Pᵀ, with no shuffle.
 //   * V reaches the matrix cores through the LDS transpose read, which hands
 //     each lane 4 consecutive keys of one head-dimension column.
-//   * Software pipelining in program order, per 32-key subtile:
-//     exponentials of this subtile, score MFMAs of the next, P·V MFMAs of
-//     this one, row max of the next -- neighbouring matrix and vector work is
-//     independent, so the two units overlap within a wave.
 //   * The softmax runs in the exp2 domain (scale·log2 e folded into one FMA
 //     per score, v_exp_f32).  The reference maximum is raised only when a
 //     row's new maximum exceeds it by more than 2^8; o and l share the
 //     reference, so o/l is unchanged and the output rescale stays off the
 //     common path.
-//   * Causal: key tiles wholly above a wave's diagonal cost that wave
-//     nothing, the mask is applied only on subtiles that cross the diagonal
-//     or the sequence end (block classification of "Masking variants",
-//     "Attention Computation in Practice" section 5), and the longest query
-//     tiles are launched first.
+//   * Causal: subtiles wholly above a wave's diagonal cost that wave nothing,
+//     the mask is applied only on subtiles that cross the diagonal or the
+//     sequence end (block classification of "Masking variants", "Attention
+//     Computation in Practice" section 5), and the longest query tiles are
+//     launched first.
 #include "device_common.hpp"
 #include "launchers.hpp"
+
+#include <type_traits>
 
 namespace attn {
 
@@ -52,25 +57,21 @@ namespace {
 // Largest growth of a row maximum (in log2 units) absorbed without rescaling.
 constexpr float kRescaleLog2 = 8.f;
 
-// Per head dimension: NB 32-row query blocks per wave and the number of LDS
-// stages.  d=64 takes two blocks (64 rows per wave) and three stages; at d=128
-// two blocks' output accumulators and Q operands alone would fill the register
-// budget of two waves per SIMD, so it takes one block and two stages.  Both run
-// two waves per SIMD, so one wave's softmax also overlaps the other's MFMAs.
+// NB 32-row query blocks per wave: two at d=64; one at d=128, where two
+// blocks' accumulators and Q operands would not fit two waves per SIMD.
 template <int D>
 struct PrefillCfg {
   static constexpr int NB = D == 64 ? 2 : 1;
-  static constexpr int WAVES = 4;
+  static constexpr int WAVES = 8;               // two groups of four, two waves per SIMD
   static constexpr int BR = 32 * NB * WAVES;    // query rows per workgroup
   static constexpr int BC = 64;                 // keys per tile (two 32-key subtiles)
   static constexpr int ROWB = 2 * D;            // bytes per K/V row
   static constexpr int CPR = D / 8;             // 16-byte chunks per row
   static constexpr int TILE = BC * ROWB;        // bytes of one K (or V) tile
   static constexpr int STAGE = 2 * TILE;        // K tile then V tile
-  static constexpr int STAGES = D == 64 ? 3 : 2;
+  static constexpr int STAGES = 4;              // LDS tile buffers
   static constexpr int LDS = STAGES * STAGE;
-  static constexpr int DMA = TILE / 16 / 256;   // 1 KB wave transfers per thread per tensor per tile
-  static constexpr int WAVES_PER_EU = 2;
+  static constexpr int DMA = TILE / 16 / (64 * WAVES);  // 1 KB transfers per wave per tensor per tile
 };
 
 // Chunk swizzles (physical 16-byte chunk = logical chunk ^ swizzle(row)).
@@ -89,17 +90,54 @@ __device__ __forceinline__ int swz_v(int r) {
 // MFMA row i of a 32-key subtile carries key perm_row(i): bits 2 and 3 swapped.
 __device__ __forceinline__ int perm_row(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
 
+// s_waitcnt vmcnt(N), other counters untouched (gfx9 field layout).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// End of a step: a workgroup barrier that nothing is scheduled across.  No
+// memory fence: buffer-to-LDS loads in flight stay in flight, their
+// completion is awaited explicitly.  A vector step also waits for this wave's
+// LDS reads, its own and those of the matrix step before it, so that once the
+// barrier opens nothing this wave read can still be pending when a later tile
+// fetch overwrites it; a matrix step leaves its reads in flight and goes
+// straight to the barrier.
+template <bool WAIT_LDS>
+__device__ __forceinline__ void step_end() {
+  __builtin_amdgcn_sched_barrier(0);  // keep the wait below the step's own work
+  if (WAIT_LDS) __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
+// Kernel-local helpers are lambdas; all of them are inlined (a call would
+// spill the operand registers to scratch memory).
+#define ATTN_INLINE __attribute__((always_inline))
+
+// Pins a value in registers at this point of the program: the empty asm
+// statement reads and rewrites it, so whatever computes the value stays before
+// it and whatever uses the result stays after.  Used at the end of each step,
+// so the compiler cannot move one step's arithmetic into the next one.
+template <class V>
+__device__ __forceinline__ void pin(V& x) {
+  asm volatile("" : "+v"(x));
+}
+
 }  // namespace
 
 template <class T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PrefillCfg<D>::WAVES_PER_EU,
-                                                                     PrefillCfg<D>::WAVES_PER_EU))) void
-prefill_fwd_kernel(const char* __restrict__ q, const char* __restrict__ k, const char* __restrict__ v,
-                   char* __restrict__ o, int batch, int hq, int hkv, int n, float c, int num_q_tiles) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_fwd_kernel(
+    const char* __restrict__ q, const char* __restrict__ k, const char* __restrict__ v, char* __restrict__ o,
+    int batch, int hq, int hkv, int n, float c, int num_q_tiles) {
   using Cfg = PrefillCfg<D>;
   constexpr int NB = Cfg::NB;
   constexpr int KK = D / 16;  // 32x32x16 k-steps over the head dimension
   constexpr int DT = D / 32;  // 32-row output tiles of the head dimension
+  constexpr int S = Cfg::STAGES;
   constexpr uint32_t ROWB = Cfg::ROWB;
   __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS];
 
@@ -108,6 +146,7 @@ prefill_fwd_kernel(const char* __restrict__ q, const char* __restrict__ k, const
   // wave-uniform by construction; readfirstlane lets the compiler keep it (and
   // the LDS-DMA destinations and buffer resources derived from it) in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;  // waves w and w+4 share a SIMD and sit in different groups
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
@@ -157,30 +196,56 @@ prefill_fwd_kernel(const char* __restrict__ q, const char* __restrict__ k, const
 
   const int kend = CAUSAL ? min(n, q0 + Cfg::BR) : n;  // keys any row of this workgroup can see
   const int nkt = (kend + Cfg::BC - 1) / Cfg::BC;
-  const int wave_last = min(n - 1, qw + 32 * NB - 1); // last live query row of this wave
 
   // ---- tile fetch: 1 KB wave transfers straight into LDS.  Transfer g = i·WAVES + wave
   // fills bytes [g·1024, g·1024 + 1024) of the tile; lane l fills slot g·64 + l, i.e.
   // physical chunk (slot % CPR) of row slot / CPR, with the logical chunk that maps there.
-  // Row / CPR arithmetic makes the swizzle of every transfer of a lane the same.
+  // Transfer groups start on multiples of 32 rows, so a lane's swizzle is the same in all.
   const int slot_row = (wave * 64 + lane) / Cfg::CPR;
   const int slot_chunk = lane % Cfg::CPR;
   const uint32_t k_src = slot_row * ROWB + ((slot_chunk ^ swz_k<D>(slot_row)) * 16);
   const uint32_t v_src = slot_row * ROWB + ((slot_chunk ^ swz_v<D>(slot_row)) * 16);
-  auto fetch_tile = [&](int it, int stage) {
-    const int j0 = min(it * Cfg::BC, n);
-    const int bytes = min(Cfg::BC, n - j0) * (int)ROWB;  // rows past the end read as 0
-    const char* kt = kp + (size_t)j0 * ROWB;
-    const char* vt = vp + (size_t)j0 * ROWB;
-    const uint32_t st = lds_addr(lds) + stage * Cfg::STAGE;
+  constexpr int PT = 2 * Cfg::DMA;  // transfers per tile per wave: part j is tensor j&1 (K, V), group j>>1
+  // Fetch cursor: scalar state of the next tile to fetch, advanced one tile at a
+  // time so that issuing a transfer costs a handful of scalar instructions.
+  int issued = 0;                                       // transfers this wave has issued so far
+  const char* f_k = kp;                                 // K row j0 of the cursor's tile
+  const char* f_v = vp;                                 // V row j0
+  uint32_t f_rem = (uint32_t)n * ROWB;                  // bytes from row j0 to the sequence end
+  const uint32_t f_dst0 = lds_addr(lds) + wave * 1024;  // this wave's transfers land at stage + g·1024
+  uint32_t f_dst = f_dst0;                              // ... of the cursor's stage
+  auto fetch_part = [&](int j) ATTN_INLINE {                        // transfer j of the cursor's tile
+    const uint32_t first = (j >> 1) * Cfg::WAVES * 1024;  // the transfer group's first byte in the tile
+    const uint32_t rec = f_rem > first ? f_rem - first : 0u;  // rows past the end read as 0
+    dma16_to_lds(bufres_words(((j & 1) ? f_v : f_k) + first, rec), (j & 1) ? v_src : k_src,
+                 f_dst + (j & 1) * Cfg::TILE + first);
+    ++issued;
+  };
+  auto fetch_advance = [&]() ATTN_INLINE {
+    f_k += Cfg::BC * ROWB;
+    f_v += Cfg::BC * ROWB;
+    f_rem = f_rem > Cfg::BC * ROWB ? f_rem - Cfg::BC * ROWB : 0u;
+    f_dst = f_dst + Cfg::STAGE == f_dst0 + S * Cfg::STAGE ? f_dst0 : f_dst + Cfg::STAGE;
+  };
+  auto fetch_tile = [&]() ATTN_INLINE {
 #pragma unroll
-    for (int i = 0; i < Cfg::DMA; ++i) {
-      const int first = i * Cfg::WAVES * 1024;          // the transfer group's first byte in the tile
-      const uint32_t off = first + wave * 1024;         // this wave's transfer
-      const int rec = bytes > first ? bytes - first : 0;
-      dma16_to_lds(bufres_words(kt + first, (uint32_t)rec), k_src, st + off);
-      dma16_to_lds(bufres_words(vt + first, (uint32_t)rec), v_src, st + Cfg::TILE + off);
-    }
+    for (int j = 0; j < PT; ++j) fetch_part(j);
+    fetch_advance();
+  };
+  // Wait until every transfer of tiles 0 .. t issued by this wave has landed:
+  // vector-memory operations complete in issue order, so at most
+  // issued - PT·(t+1) may stay in flight (a smaller count only waits longer).
+  auto wait_tile = [&](int t) ATTN_INLINE {
+    const int pending = issued - PT * (t + 1);
+    if (pending <= 0) wait_vm<0>();
+    else if (pending == 1) wait_vm<1>();
+    else if (pending == 2) wait_vm<2>();
+    else if (pending == 3) wait_vm<3>();
+    else if (pending == 4) wait_vm<4>();
+    else if (pending == 5) wait_vm<5>();
+    else if (pending == 6) wait_vm<6>();
+    else if (pending == 7) wait_vm<7>();
+    else wait_vm<8>();
   };
 
   // ---- per-lane LDS read offsets (within a stage)
@@ -214,32 +279,97 @@ prefill_fwd_kernel(const char* __restrict__ q, const char* __restrict__ k, const
   for (int blk = 0; blk < NB; ++blk) {
     m_run[blk] = kNegInf;
     l_run[blk] = 0.f;
-  }
-#pragma unroll
-  for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) oacc[blk][dt][e] = 0.f;
+  }
 
-  // scores of subtile sb of the tile in `stage`: s[blk][e] is key
-  // 16·(e>>3) + 8·half + (e&7) of the subtile against query qw + 32·blk + l32
-  auto qk = [&](f32x16 (&s)[NB], int stage, int sb) {
-    const char* st = lds + stage * Cfg::STAGE + sb * 32 * ROWB;
+  // Operands staged in registers one step ahead of the matrix step that uses them.
+  u32x4 kf[KK];      // K of the next score subtile
+  u32x4 vf[DT][2];   // V of the next P·V subtile, per output tile and 16-key k-step
+  f32x16 s[NB];      // scores of one subtile: s[blk][e] is key 16·(e>>3) + 8·half + (e&7)
+                     // of the subtile against query qw + 32·blk + l32
+  u32x4 pf[NB][2];   // probabilities of one subtile, B operands of P·V
+
+  auto subtile = [&](int t, int sb) ATTN_INLINE { return lds + (t % S) * Cfg::STAGE + sb * 32 * ROWB; };
+  auto load_k = [&](int t, int sb) ATTN_INLINE {
+    const char* st = subtile(t, sb);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) kf[kk] = lds_read16(st, k_rd[kk]);
+  };
+  auto load_v = [&](int t, int sb) ATTN_INLINE {
+    const char* st = subtile(t, sb);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const u32x2 va = lds_read_tr16(st + ks * 16 * ROWB, v_rd[dt][0]);
+        const u32x2 vb = lds_read_tr16(st + ks * 16 * ROWB, v_rd[dt][1]);
+        vf[dt][ks] = u32x4{va[0], va[1], vb[0], vb[1]};
+      }
+  };
+
+  auto qk = [&]() ATTN_INLINE {
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[blk][e] = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const u32x4 kf = lds_read16(st, k_rd[kk]);
+    for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-      for (int blk = 0; blk < NB; ++blk) s[blk] = T::mfma32(kf, qf[blk][kk], s[blk]);
-    }
+      for (int blk = 0; blk < NB; ++blk) s[blk] = T::mfma32(kf[kk], qf[blk][kk], s[blk]);
   };
 
-  // mask, row max and (rarely) the rescale of one subtile's scores starting at key s0
-  auto row_max = [&](f32x16 (&s)[NB], int s0) {
+  auto pv = [&]() ATTN_INLINE {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) oacc[blk][dt] = T::mfma32(vf[dt][ks], pf[blk][ks], oacc[blk][dt]);
+  };
+  // P·V of the staged V operand while the V operand of subtile sb of tile t is
+  // read into the same registers, each fragment right after its last use
+  auto pv_load_v = [&](int t, int sb) ATTN_INLINE {
+    const char* st = subtile(t, sb);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) oacc[blk][dt] = T::mfma32(vf[dt][ks], pf[blk][ks], oacc[blk][dt]);
+        const u32x2 va = lds_read_tr16(st + ks * 16 * ROWB, v_rd[dt][0]);
+        const u32x2 vb = lds_read_tr16(st + ks * 16 * ROWB, v_rd[dt][1]);
+        vf[dt][ks] = u32x4{va[0], va[1], vb[0], vb[1]};
+        __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);  // the MFMA(s) ...
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // ... then the two reads
+      }
+  };
+  // probabilities of the subtile starting at key s0, rounded to the storage
+  // type as the B operands of P·V, and their row sums.  The exponentials use the
+  // current reference maximum m_run while the subtile's row maximum is found
+  // alongside; only if some row's maximum exceeds the reference by more than
+  // kRescaleLog2 (always on a row's first live subtile) is the reference raised
+  // -- l and o rescaled by exp2(m_run - m_new), which is 0 while m_run = -inf --
+  // and the subtile's probabilities recomputed.  o and l share the reference,
+  // so o/l is the same either way.
+  auto pack_sum = [&](int blk, const float (&p)[16]) {
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pf[blk][ks][i] = T::pack2(p[8 * ks + 2 * i], p[8 * ks + 2 * i + 1]);
+        ps[i] = T::add_pair(ps[i], pf[blk][ks][i]);
+      }
+    return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  };
+  auto exps = [&](int blk, float ref, float (&p)[16]) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) p[e] = fast_exp2(fmaf(s[blk][e], c, -ref));
+  };
+  auto softmax = [&](int s0) ATTN_INLINE {
     if (s0 + 32 > n || (CAUSAL && s0 + 31 > qw)) {
 #pragma unroll
       for (int blk = 0; blk < NB; ++blk) {
@@ -251,126 +381,138 @@ prefill_fwd_kernel(const char* __restrict__ q, const char* __restrict__ k, const
         }
       }
     }
-    float m_tile[NB];
+    float rsum[NB], m_tile[NB];
     bool grow = false;
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
-      float mx = fmaxf(s[blk][0], s[blk][1]);
+      float p[16];
+      exps(blk, m_run[blk] == kNegInf ? 0.f : m_run[blk], p);
+      rsum[blk] = pack_sum(blk, p);
+      float m3[6];
 #pragma unroll
-      for (int e = 2; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s[blk][e], s[blk][e + 1]));
+      for (int i = 0; i < 5; ++i) m3[i] = fmaxf(fmaxf(s[blk][3 * i], s[blk][3 * i + 1]), s[blk][3 * i + 2]);
+      m3[5] = s[blk][15];
+      const float mx = fmaxf(fmaxf(fmaxf(m3[0], m3[1]), m3[2]), fmaxf(fmaxf(m3[3], m3[4]), m3[5]));
       m_tile[blk] = max_xor32(mx) * c;
       grow |= m_tile[blk] > m_run[blk] + kRescaleLog2;
     }
-    // Raise the reference maximum only when some row's new maximum exceeds it
-    // by more than kRescaleLog2 (always on a row's first live subtile); l and o
-    // are rescaled by exp2(m_run - m_new), which is 0 while m_run = -inf.
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
       for (int blk = 0; blk < NB; ++blk) {
         const float m_new = fmaxf(m_run[blk], m_tile[blk]);
-        const float alpha = fast_exp2(m_run[blk] - (m_new == kNegInf ? 0.f : m_new));
+        const float ref = m_new == kNegInf ? 0.f : m_new;  // a row with no live key stays empty
+        const float alpha = fast_exp2(m_run[blk] - ref);
         l_run[blk] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) oacc[blk][dt] *= alpha;
         m_run[blk] = m_new;
+        float p[16];
+        exps(blk, ref, p);
+        rsum[blk] = pack_sum(blk, p);
       }
     }
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) l_run[blk] += rsum[blk];
   };
 
-  // probabilities rounded to the storage type as the B operands of P·V (one per
-  // 16-key k-step), and their row sums
-  auto exp_pack = [&](f32x16 (&s)[NB], u32x4 (&pf)[NB][2]) {
+  // results of a vector step (probabilities and running statistics) and of a
+  // matrix step (scores and output accumulators)
+  auto pin_vector_step = [&]() ATTN_INLINE {
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
-      const float m_use = (m_run[blk] == kNegInf) ? 0.f : m_run[blk];  // a row with no live key stays empty
+      pin(pf[blk][0]);
+      pin(pf[blk][1]);
+      pin(l_run[blk]);
+      pin(m_run[blk]);
+    }
+  };
+  auto pin_matrix_step = [&]() ATTN_INLINE {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[blk][e] = fast_exp2(fmaf(s[blk][e], c, -m_use));
-      float ps0 = 0.f, ps1 = 0.f;
+    for (int blk = 0; blk < NB; ++blk) {
+      pin(s[blk]);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pf[blk][ks][i] = T::pack2(s[blk][8 * ks + 2 * i], s[blk][8 * ks + 2 * i + 1]);
-          if (i & 1)
-            ps1 = T::add_pair(ps1, pf[blk][ks][i]);
-          else
-            ps0 = T::add_pair(ps0, pf[blk][ks][i]);
-        }
-      l_run[blk] += ps0 + ps1;
+      for (int dt = 0; dt < DT; ++dt) pin(oacc[blk][dt]);
     }
   };
 
-  auto pv = [&](const u32x4 (&pf)[NB][2], int stage, int sb) {
-    const char* st = lds + stage * Cfg::STAGE + sb * 32 * ROWB;
+  // ---- the steps of one wave, for subtiles u = 2t (sb 0) and 2t+1 (sb 1) of tile t:
+  //   step 0      matrix  scores of subtile 0 (K read here); read V of 0
+  //   step 4t+1   vector  softmax of 2t;   read K of 2t+1
+  //   step 4t+2   matrix  scores of 2t+1, P·V of 2t;   read V of 2t+1
+  //   step 4t+3   vector  softmax of 2t+1; read K of 2t+2
+  //   step 4t+4   matrix  scores of 2t+2, P·V of 2t+1; read V of 2t+2
+  // so each group's LDS reads are split evenly between its two kinds of step,
+  // and tile t is read by steps 4t-1 .. 4t+2 (0 .. 2 for tile 0).  Every step
+  // ends at a workgroup barrier.  Group 1 passes one extra barrier first, so it
+  // runs each step one phase after group 0: on every SIMD one wave is in a
+  // matrix step while the other is in a vector step.
+  //
+  // Tiles 0 .. S-1 are fetched up front.  Tile t+S-1 (t >= 1) is fetched one
+  // transfer per step during steps 4t+1 .. 4t+4; its buffer last held tile t-1,
+  // whose final read (group 1, step 4t-2) has returned by the end of group 1's
+  // vector step 4t-1, i.e. before the barrier that opens group 0's step 4t+1.  Each wave waits for its transfers of tile t+1 at the end
+  // of step 4t+1, before the barriers that precede group 0's first read of it
+  // (step 4t+3).
+  static_assert(S >= 3, "the fetch schedule needs three tile buffers");
+  static_assert(PT % 2 == 0 && PT <= 4, "transfers split evenly over the two matrix steps of a tile");
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+  for (int t = 0; t < S; ++t)
+    if (t < nkt) fetch_tile();
+  wait_vm<0>();  // Q operands and the first tiles
+  step_end<true>();
+  if (grp == 1) step_end<true>();
+
+  load_k(0, 0);
+  qk();
+  load_v(0, 0);
+  pin_matrix_step();
+  step_end<false>();
+  // Transfers of the tile being fetched, issued after a matrix step's score
+  // MFMAs so the matrix core has queued work while they go out.
+  auto fetch_half = [&](bool fetch, int h) ATTN_INLINE {
+    __builtin_amdgcn_sched_barrier(0);
+    if (fetch) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const u32x2 va = lds_read_tr16(st + ks * 16 * ROWB, v_rd[dt][0]);
-        const u32x2 vb = lds_read_tr16(st + ks * 16 * ROWB, v_rd[dt][1]);
-        const u32x4 vf = {va[0], va[1], vb[0], vb[1]};
-#pragma unroll
-        for (int blk = 0; blk < NB; ++blk) oacc[blk][dt] = T::mfma32(vf, pf[blk][ks], oacc[blk][dt]);
-      }
+      for (int j = h * PT / 2; j < (h + 1) * PT / 2; ++j) fetch_part(j);
+      if (h == 1) fetch_advance();
+    }
+    __builtin_amdgcn_sched_barrier(0);
   };
-
-  // ---- pipeline.  Invariant at the top of a tile step: the tile is in LDS and
-  // visible, the next tile is in flight, and `s` holds the (masked, max-applied)
-  // scores of this tile's subtile 0.
-  f32x16 s[NB], s_next[NB];
-  u32x4 pf[NB][2];
-
-  fetch_tile(0, 0);
-  wait_vm_all();
-  __syncthreads();
-  if (nkt > 1) fetch_tile(1, 1);
-  bool live = !CAUSAL || 0 <= wave_last;
-  if (live) {
-    qk(s, 0, 0);
-    row_max(s, 0);
-  }
-
-  auto tile_step = [&](int it, int stage) {
-    const int j0 = it * Cfg::BC;
-    const bool live0 = !CAUSAL || j0 <= wave_last;
-    const bool live1 = !CAUSAL || j0 + 32 <= wave_last;
-    // subtile 0: exponentials, next subtile's scores, this subtile's P·V
-    if (live0) {
-      exp_pack(s, pf);
-      if (live1) qk(s_next, stage, 1);
-      pv(pf, stage, 0);
-      if (live1) row_max(s_next, j0 + 32);
+  // one tile; the last one has no successor to read or score
+  auto tile_steps = [&](int t, auto last_tag) ATTN_INLINE {
+    constexpr bool LAST = decltype(last_tag)::value;
+    const bool fetch = t >= 1 && t + S - 1 < nkt;
+    // step 4t+1: softmax of subtile 2t; K of 2t+1
+    load_k(t, 1);
+    softmax(64 * t);
+    if (!LAST) wait_tile(t + 1);
+    pin_vector_step();
+    step_end<true>();
+    // step 4t+2: scores of 2t+1, P·V of 2t; V of 2t+1
+    qk();
+    fetch_half(fetch, 0);
+    pv_load_v(t, 1);
+    pin_matrix_step();
+    step_end<false>();
+    // step 4t+3: softmax of 2t+1; K of 2t+2
+    if (!LAST) load_k(t + 1, 0);
+    softmax(64 * t + 32);
+    pin_vector_step();
+    step_end<true>();
+    // step 4t+4: scores of 2t+2, P·V of 2t+1; V of 2t+2
+    if (LAST) {
+      pv();
+    } else {
+      qk();
+      fetch_half(fetch, 1);
+      pv_load_v(t + 1, 0);
     }
-    // subtile 1 and the hand-over to the next tile.  With three stages the
-    // next tile's first scores are issued before this subtile's P·V (its stage
-    // is not refilled until the next barrier); with two, this tile's stage is
-    // refilled right after the barrier, so its P·V must come first.
-    const int nstage = (stage + 1) % Cfg::STAGES;
-    const bool more = it + 1 < nkt;
-    const bool live2 = more && (!CAUSAL || j0 + 64 <= wave_last);
-    if (live1) exp_pack(s_next, pf);
-    if (Cfg::STAGES == 2 && live1) pv(pf, stage, 1);
-    if (more) {
-      wait_vm_all();   // the next tile has landed (this wave's part)
-      __syncthreads(); // ... everyone's part; every wave is past its last read of the stage refilled next
-      if (it + 2 < nkt) fetch_tile(it + 2, (stage + 2) % Cfg::STAGES);
-      if (live2) qk(s, nstage, 0);
-    }
-    if (Cfg::STAGES == 3 && live1) pv(pf, stage, 1);
-    if (live2) row_max(s, j0 + 64);
+    pin_matrix_step();
+    step_end<false>();
   };
-
-  // unrolled by the stage count so each stage is a compile-time constant
-  for (int it = 0;;) {
-    tile_step(it, 0);
-    if (++it >= nkt) break;
-    tile_step(it, 1);
-    if (++it >= nkt) break;
-    if (Cfg::STAGES == 3) {
-      tile_step(it, 2);
-      if (++it >= nkt) break;
-    }
-  }
+  for (int t = 0; t + 1 < nkt; ++t) tile_steps(t, std::false_type{});
+  tile_steps(nkt - 1, std::true_type{});
+  if (grp == 0) step_end<true>();
 
   // ---- epilogue: O = o / l, rounded to the storage type, written once
 #pragma unroll
@@ -399,7 +541,7 @@ static hipError_t launch_prefill_t(const void* q, const void* k, const void* v, 
   using Cfg = PrefillCfg<D>;
   const int tiles = (n + Cfg::BR - 1) / Cfg::BR;
   const long long blocks = (long long)tiles * hq * batch;
-  prefill_fwd_kernel<T, D, CAUSAL><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
+  prefill_fwd_kernel<T, D, CAUSAL><<<dim3((unsigned)blocks), dim3(64 * Cfg::WAVES), 0, stream>>>(
       static_cast<const char*>(q), static_cast<const char*>(k), static_cast<const char*>(v), static_cast<char*>(o),
       batch, hq, hkv, n, scale * kLog2e, tiles);
   return hipGetLastError();
