@@ -54,8 +54,10 @@ namespace attn {
 
 namespace {
 
-// Largest growth of a row maximum (in log2 units) absorbed without rescaling.
+// Largest probability (as a power of two) used without raising the reference
+// maximum, and the matching bound on a lane's 16-key probability sum.
 constexpr float kRescaleLog2 = 8.f;
+constexpr float kRescaleSum = 256.f;  // 2^kRescaleLog2
 
 // NB 32-row query blocks per wave: two at d=64; one at d=128, where two
 // blocks' accumulators and Q operands would not fit two waves per SIMD.
@@ -348,26 +350,32 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
   // probabilities of the subtile starting at key s0, rounded to the storage
   // type as the B operands of P·V, and their row sums.  The exponentials use the
-  // current reference maximum m_run while the subtile's row maximum is found
-  // alongside; only if some row's maximum exceeds the reference by more than
-  // kRescaleLog2 (always on a row's first live subtile) is the reference raised
-  // -- l and o rescaled by exp2(m_run - m_new), which is 0 while m_run = -inf --
-  // and the subtile's probabilities recomputed.  o and l share the reference,
-  // so o/l is the same either way.
-  auto pack_sum = [&](int blk, const float (&p)[16]) {
+  // current reference m_run (the largest row maximum seen when it was last
+  // raised).  The reference is raised -- to the row maximum so far, with l and
+  // o rescaled by exp2(m_run - m_new) -- and the subtile recomputed only when
+  // some lane's 16 probabilities sum past 2^kRescaleLog2, or on a row's first
+  // subtile (no reference yet).  Every probability used is therefore at most
+  // 2^kRescaleLog2 and the row maximum is at most kRescaleLog2 above the
+  // reference, so nothing overflows or loses precision; o and l share the
+  // reference, so o/l is the same either way.
+  float neg_ref[NB], lim[NB];  // -m_run (0 while m_run = -inf); the row-sum limit (-1 forces a raise)
+#pragma unroll
+  for (int blk = 0; blk < NB; ++blk) {
+    neg_ref[blk] = 0.f;
+    lim[blk] = -1.f;
+  }
+  auto probs = [&](int blk, float nref) ATTN_INLINE {  // returns this lane's sum of the 16 rounded probabilities
     float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        pf[blk][ks][i] = T::pack2(p[8 * ks + 2 * i], p[8 * ks + 2 * i + 1]);
+        const float a0 = fast_exp2(fmaf(s[blk][8 * ks + 2 * i], c, nref));
+        const float a1 = fast_exp2(fmaf(s[blk][8 * ks + 2 * i + 1], c, nref));
+        pf[blk][ks][i] = T::pack2(a0, a1);
         ps[i] = T::add_pair(ps[i], pf[blk][ks][i]);
       }
     return (ps[0] + ps[1]) + (ps[2] + ps[3]);
-  };
-  auto exps = [&](int blk, float ref, float (&p)[16]) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) p[e] = fast_exp2(fmaf(s[blk][e], c, -ref));
   };
   auto softmax = [&](int s0) ATTN_INLINE {
     if (s0 + 32 > n || (CAUSAL && s0 + 31 > qw)) {
@@ -381,38 +389,35 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
       }
     }
-    float rsum[NB], m_tile[NB];
+    float psum[NB];
     bool grow = false;
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
-      float p[16];
-      exps(blk, m_run[blk] == kNegInf ? 0.f : m_run[blk], p);
-      rsum[blk] = pack_sum(blk, p);
-      float m3[6];
-#pragma unroll
-      for (int i = 0; i < 5; ++i) m3[i] = fmaxf(fmaxf(s[blk][3 * i], s[blk][3 * i + 1]), s[blk][3 * i + 2]);
-      m3[5] = s[blk][15];
-      const float mx = fmaxf(fmaxf(fmaxf(m3[0], m3[1]), m3[2]), fmaxf(fmaxf(m3[3], m3[4]), m3[5]));
-      m_tile[blk] = max_xor32(mx) * c;
-      grow |= m_tile[blk] > m_run[blk] + kRescaleLog2;
+      psum[blk] = probs(blk, neg_ref[blk]);
+      grow |= !(psum[blk] <= lim[blk]);  // also true for an infinite or NaN sum
     }
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
       for (int blk = 0; blk < NB; ++blk) {
-        const float m_new = fmaxf(m_run[blk], m_tile[blk]);
+        float m3[6];
+#pragma unroll
+        for (int i = 0; i < 5; ++i) m3[i] = fmaxf(fmaxf(s[blk][3 * i], s[blk][3 * i + 1]), s[blk][3 * i + 2]);
+        m3[5] = s[blk][15];
+        const float mx = fmaxf(fmaxf(fmaxf(m3[0], m3[1]), m3[2]), fmaxf(fmaxf(m3[3], m3[4]), m3[5]));
+        const float m_new = fmaxf(m_run[blk], max_xor32(mx) * c);
         const float ref = m_new == kNegInf ? 0.f : m_new;  // a row with no live key stays empty
         const float alpha = fast_exp2(m_run[blk] - ref);
         l_run[blk] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) oacc[blk][dt] *= alpha;
         m_run[blk] = m_new;
-        float p[16];
-        exps(blk, ref, p);
-        rsum[blk] = pack_sum(blk, p);
+        neg_ref[blk] = -ref;
+        lim[blk] = m_new == kNegInf ? -1.f : kRescaleSum;
+        psum[blk] = probs(blk, -ref);
       }
     }
 #pragma unroll
-    for (int blk = 0; blk < NB; ++blk) l_run[blk] += rsum[blk];
+    for (int blk = 0; blk < NB; ++blk) l_run[blk] += psum[blk];
   };
 
   // results of a vector step (probabilities and running statistics) and of a
@@ -424,6 +429,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       pin(pf[blk][1]);
       pin(l_run[blk]);
       pin(m_run[blk]);
+      pin(neg_ref[blk]);
+      pin(lim[blk]);
     }
   };
   auto pin_matrix_step = [&]() ATTN_INLINE {
