@@ -347,7 +347,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);  // the MFMA(s) ...
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // ... then the two reads
       }
+  };  // The next V operand is read between the P·V MFMAs at d=128; at d=64, whose
+  // vector steps are the longer ones, after all of the step's MFMAs (measured).
+  auto pv_then_load_v = [&](int t, int sb) ATTN_INLINE {
+    if (D == 64) {
+      pv();
+      __builtin_amdgcn_sched_barrier(0);
+      load_v(t, sb);
+    } else {
+      pv_load_v(t, sb);
+    }
   };
+
   // probabilities of the subtile starting at key s0, rounded to the storage
   // type as the B operands of P·V, and their row sums.  The exponentials use the
   // current reference m_run (the largest row maximum seen when it was last
@@ -454,14 +465,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // runs each step one phase after group 0: on every SIMD one wave is in a
   // matrix step while the other is in a vector step.
   //
-  // Tiles 0 .. S-1 are fetched up front.  Tile t+S-1 (t >= 1) is fetched one
-  // transfer per step during steps 4t+1 .. 4t+4; its buffer last held tile t-1,
-  // whose final read (group 1, step 4t-2) has returned by the end of group 1's
-  // vector step 4t-1, i.e. before the barrier that opens group 0's step 4t+1.  Each wave waits for its transfers of tile t+1 at the end
-  // of step 4t+1, before the barriers that precede group 0's first read of it
-  // (step 4t+3).
+  // Tiles 0 .. S-1 are fetched up front.  Tile t+S-1 (t >= 1) is fetched at the
+  // start of vector steps 4t+1 and 4t+3, half of its transfers each; its buffer
+  // last held tile t-1, whose final read (group 1, step 4t-2) has returned by
+  // the end of group 1's vector step 4t-1, i.e. before the barrier that opens
+  // group 0's step 4t+1.  Each wave waits for its transfers of tile t+1 at the
+  // end of step 4t+1, before the barriers that precede group 0's first read of
+  // it (step 4t+3).
   static_assert(S >= 3, "the fetch schedule needs three tile buffers");
-  static_assert(PT % 2 == 0 && PT <= 4, "transfers split evenly over the two matrix steps of a tile");
+  static_assert(PT % 2 == 0 && PT <= 4, "transfers split evenly over the two vector steps of a tile");
 #pragma unroll
   for (int t = 0; t < S; ++t)
     if (t < nkt) fetch_tile();
@@ -474,8 +486,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   load_v(0, 0);
   pin_matrix_step();
   step_end<false>();
-  // Transfers of the tile being fetched, issued after a matrix step's score
-  // MFMAs so the matrix core has queued work while they go out.
+  // Transfers of the tile being fetched, issued at the start of a vector step
+  // (measured: issued inside a matrix step they can hold up its MFMAs).
   auto fetch_half = [&](bool fetch, int h) ATTN_INLINE {
     __builtin_amdgcn_sched_barrier(0);
     if (fetch) {
@@ -490,6 +502,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr bool LAST = decltype(last_tag)::value;
     const bool fetch = t >= 1 && t + S - 1 < nkt;
     // step 4t+1: softmax of subtile 2t; K of 2t+1
+    fetch_half(fetch, 0);
     load_k(t, 1);
     softmax(64 * t);
     if (!LAST) wait_tile(t + 1);
@@ -497,11 +510,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     step_end<true>();
     // step 4t+2: scores of 2t+1, P·V of 2t; V of 2t+1
     qk();
-    fetch_half(fetch, 0);
-    pv_load_v(t, 1);
+    pv_then_load_v(t, 1);
     pin_matrix_step();
     step_end<false>();
     // step 4t+3: softmax of 2t+1; K of 2t+2
+    fetch_half(fetch, 1);
     if (!LAST) load_k(t + 1, 0);
     softmax(64 * t + 32);
     pin_vector_step();
@@ -511,8 +524,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       pv();
     } else {
       qk();
-      fetch_half(fetch, 1);
-      pv_load_v(t + 1, 0);
+      pv_then_load_v(t + 1, 0);
     }
     pin_matrix_step();
     step_end<false>();
