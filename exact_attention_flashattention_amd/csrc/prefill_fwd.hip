@@ -70,9 +70,9 @@ struct PrefillCfg {
   static constexpr int ROWB = 2 * D;            // bytes per K/V row
   static constexpr int CPR = D / 8;             // 16-byte chunks per row
   static constexpr int TILE = BC * ROWB;        // bytes of one K (or V) tile
-  static constexpr int STAGE = 2 * TILE;        // K tile then V tile
   static constexpr int STAGES = 4;              // LDS tile buffers
-  static constexpr int LDS = STAGES * STAGE;
+  static constexpr int VREG = STAGES * TILE;    // K tiles of all buffers first, then the V tiles
+  static constexpr int LDS = 2 * VREG;
   static constexpr int DMA = TILE / 16 / (64 * WAVES);  // 1 KB transfers per wave per tensor per tile
 };
 
@@ -220,14 +220,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const uint32_t first = (j >> 1) * Cfg::WAVES * 1024;  // the transfer group's first byte in the tile
     const uint32_t rec = f_rem > first ? f_rem - first : 0u;  // rows past the end read as 0
     dma16_to_lds(bufres_words(((j & 1) ? f_v : f_k) + first, rec), (j & 1) ? v_src : k_src,
-                 f_dst + (j & 1) * Cfg::TILE + first);
+                 f_dst + (j & 1) * Cfg::VREG + first);
     ++issued;
   };
   auto fetch_advance = [&]() ATTN_INLINE {
     f_k += Cfg::BC * ROWB;
     f_v += Cfg::BC * ROWB;
     f_rem = f_rem > Cfg::BC * ROWB ? f_rem - Cfg::BC * ROWB : 0u;
-    f_dst = f_dst + Cfg::STAGE == f_dst0 + S * Cfg::STAGE ? f_dst0 : f_dst + Cfg::STAGE;
+    f_dst = f_dst + Cfg::TILE == f_dst0 + S * Cfg::TILE ? f_dst0 : f_dst + Cfg::TILE;
   };
   auto fetch_tile = [&]() ATTN_INLINE {
 #pragma unroll
@@ -270,7 +270,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const int lc = dt * 4 + 2 * (G & 1) + ((j & 3) >> 1);
-        v_rd[dt][p] = Cfg::TILE + r * ROWB + ((lc ^ swz_v<D>(r)) * 16) + 8 * (j & 1);
+        v_rd[dt][p] = Cfg::VREG + r * ROWB + ((lc ^ swz_v<D>(r)) * 16) + 8 * (j & 1);
       }
     }
   }
@@ -294,14 +294,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                      // of the subtile against query qw + 32·blk + l32
   u32x4 pf[NB][2];   // probabilities of one subtile, B operands of P·V
 
-  auto subtile = [&](int t, int sb) ATTN_INLINE { return lds + (t % S) * Cfg::STAGE + sb * 32 * ROWB; };
-  auto load_k = [&](int t, int sb) ATTN_INLINE {
-    const char* st = subtile(t, sb);
+  // LDS buffer ("stage") of a tile: an int, or a std::integral_constant where
+  // the loop is unrolled so that the stage offset folds into the instructions'
+  // 16-bit address offsets.  Buffer b holds its K tile at b·TILE and its V tile
+  // at VREG + b·TILE, so every such offset stays below 64 KB.
+  auto subtile = [&](auto stg, int sb) ATTN_INLINE { return lds + (int)stg * Cfg::TILE + sb * 32 * ROWB; };
+  auto next_stage = [&](auto stg) ATTN_INLINE {
+    if constexpr (std::is_same<decltype(stg), int>::value)
+      return stg + 1 == S ? 0 : stg + 1;
+    else
+      return std::integral_constant<int, (decltype(stg)::value + 1) % S>{};
+  };
+  auto load_k = [&](auto stg, int sb) ATTN_INLINE {
+    const char* st = subtile(stg, sb);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) kf[kk] = lds_read16(st, k_rd[kk]);
   };
-  auto load_v = [&](int t, int sb) ATTN_INLINE {
-    const char* st = subtile(t, sb);
+  auto load_v = [&](auto stg, int sb) ATTN_INLINE {
+    const char* st = subtile(stg, sb);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -333,8 +343,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
   // P·V of the staged V operand while the V operand of subtile sb of tile t is
   // read into the same registers, each fragment right after its last use
-  auto pv_load_v = [&](int t, int sb) ATTN_INLINE {
-    const char* st = subtile(t, sb);
+  auto pv_load_v = [&](auto stg, int sb) ATTN_INLINE {
+    const char* st = subtile(stg, sb);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -349,13 +359,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
   };  // The next V operand is read between the P·V MFMAs at d=128; at d=64, whose
   // vector steps are the longer ones, after all of the step's MFMAs (measured).
-  auto pv_then_load_v = [&](int t, int sb) ATTN_INLINE {
+  auto pv_then_load_v = [&](auto stg, int sb) ATTN_INLINE {
     if (D == 64) {
       pv();
       __builtin_amdgcn_sched_barrier(0);
-      load_v(t, sb);
+      load_v(stg, sb);
     } else {
-      pv_load_v(t, sb);
+      pv_load_v(stg, sb);
     }
   };
 
@@ -474,16 +484,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // it (step 4t+3).
   static_assert(S >= 3, "the fetch schedule needs three tile buffers");
   static_assert(PT % 2 == 0 && PT <= 4, "transfers split evenly over the two vector steps of a tile");
-#pragma unroll
-  for (int t = 0; t < S; ++t)
-    if (t < nkt) fetch_tile();
-  wait_vm<0>();  // Q operands and the first tiles
+  fetch_tile();
+  wait_vm<0>();  // Q operands and tile 0
   step_end<true>();
+#pragma unroll
+  for (int t = 1; t < S; ++t)  // in flight during the first steps
+    if (t < nkt) fetch_tile();
   if (grp == 1) step_end<true>();
 
-  load_k(0, 0);
+  load_k(std::integral_constant<int, 0>{}, 0);
   qk();
-  load_v(0, 0);
+  load_v(std::integral_constant<int, 0>{}, 0);
   pin_matrix_step();
   step_end<false>();
   // Transfers of the tile being fetched, issued at the start of a vector step
@@ -498,24 +509,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __builtin_amdgcn_sched_barrier(0);
   };
   // one tile; the last one has no successor to read or score
-  auto tile_steps = [&](int t, auto last_tag) ATTN_INLINE {
+  auto tile_steps = [&](int t, auto stg, auto last_tag) ATTN_INLINE {
     constexpr bool LAST = decltype(last_tag)::value;
     const bool fetch = t >= 1 && t + S - 1 < nkt;
     // step 4t+1: softmax of subtile 2t; K of 2t+1
     fetch_half(fetch, 0);
-    load_k(t, 1);
+    load_k(stg, 1);
     softmax(64 * t);
     if (!LAST) wait_tile(t + 1);
     pin_vector_step();
     step_end<true>();
     // step 4t+2: scores of 2t+1, P·V of 2t; V of 2t+1
     qk();
-    pv_then_load_v(t, 1);
+    pv_then_load_v(stg, 1);
     pin_matrix_step();
     step_end<false>();
     // step 4t+3: softmax of 2t+1; K of 2t+2
     fetch_half(fetch, 1);
-    if (!LAST) load_k(t + 1, 0);
+    if (!LAST) load_k(next_stage(stg), 0);
     softmax(64 * t + 32);
     pin_vector_step();
     step_end<true>();
@@ -524,13 +535,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       pv();
     } else {
       qk();
-      pv_then_load_v(t + 1, 0);
+      pv_then_load_v(next_stage(stg), 0);
     }
     pin_matrix_step();
     step_end<false>();
   };
-  for (int t = 0; t + 1 < nkt; ++t) tile_steps(t, std::false_type{});
-  tile_steps(nkt - 1, std::true_type{});
+  // groups of S tiles (none of them the last) with compile-time stages, then
+  // the remaining tiles with run-time stages
+  auto group = [&](auto self, int t0, auto j) ATTN_INLINE {
+    tile_steps(t0 + decltype(j)::value, j, std::false_type{});
+    if constexpr (decltype(j)::value + 1 < S) self(self, t0, std::integral_constant<int, decltype(j)::value + 1>{});
+  };
+  int t = 0;
+  for (; t + S < nkt; t += S) group(group, t, std::integral_constant<int, 0>{});
+  for (; t + 1 < nkt; ++t) tile_steps(t, t % S, std::false_type{});
+  tile_steps(nkt - 1, (nkt - 1) % S, std::true_type{});
   if (grp == 0) step_end<true>();
 
   // ---- epilogue: O = o / l, rounded to the storage type, written once
