@@ -21,6 +21,12 @@ dominant (longest-running) kernel, ``kernels`` lists all of them.  Inputs
 alternate between two copies so no launch finds the previous one's data in the
 last-level cache.
 
+After the step, the same decode is timed once more over a paged copy of the
+cache (16-row pages in a seeded random order, ``attn_decode_splitk_paged`` then
+``attn_merge_partials``) in a region of its own; it is reported beside the
+step (``decode_paged``, and in ``kernels``) and is not part of ``value`` or
+``ms_per_step``.
+
 ``cpu_baseline`` times the fp64 oracle on a bounded sample of the same prefill
 workload (whole heads until about ``--cpu-seconds`` have passed), on the host
 cores, as a reported baseline only.
@@ -47,6 +53,7 @@ PEAK_MFMA_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E peak
 PREFILL = ["prefill_b4_h32_n4096_d64_bf16", "prefill_b4_h32_n4096_d128_bf16"]
 DECODE = "decode_b1_hq32_hkv8_d128_len262144_bf16"
+PAGE_SIZE = 16
 CSRC = os.path.join(ROOT, "exact_attention_flashattention_amd", "csrc")
 KERNEL_SOURCES = {
     "prefill_fwd_kernel": ["prefill_fwd.hip", "device_common.hpp"],
@@ -134,7 +141,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "prefill_d64", "prefill_d128", "decode"], default="all",
+    ap.add_argument("--only", choices=["all", "prefill_d64", "prefill_d128", "decode", "decode_paged"], default="all",
                     help="run only one kernel family (for profiler runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of the bench, run plain device copies of this many MiB (counter calibration)")
@@ -169,6 +176,7 @@ def main() -> int:
     K, W = args.steps, args.warmup
     run_prefill = [n for n in PREFILL if args.only in ("all", "prefill_d" + n.split("_d")[1].split("_")[0])]
     run_decode = args.only in ("all", "decode")
+    run_paged = args.only in ("all", "decode_paged")
 
     # ---- inputs (two copies each), outputs and workspaces: all allocated before timing
     pre = []
@@ -191,6 +199,21 @@ def main() -> int:
         out = torch.empty((w.batch, w.hq, w.d), dtype=torch.bfloat16, device=dev)
         total_len = int(sum(int(c[3].sum()) for c in copies[:1]))
         dec = (w, copies, S, part, out, total_len)
+    pag = None
+    if run_paged:
+        w = workloads.WORKLOADS[DECODE]
+        copies = []
+        for s in (0, 1):
+            q, kc, vc, lens = workloads.decode_inputs(w, device=dev, salt=s)
+            kp, vp, table = workloads.paged_from_cache(kc, vc, lens, PAGE_SIZE, workloads.seed_for(w.name, "pages", s))
+            del kc, vc
+            copies.append((q, kp, vp, table.to(dev), lens.to(dev)))
+        S = A.decode_num_splits(w.batch, w.hkv, copies[0][3].shape[1] * PAGE_SIZE)
+        part = (torch.empty((w.batch, w.hq, S), dtype=torch.float32, device=dev),
+                torch.empty((w.batch, w.hq, S), dtype=torch.float32, device=dev),
+                torch.empty((w.batch, w.hq, S, w.d), dtype=torch.float32, device=dev))
+        out = torch.empty((w.batch, w.hq, w.d), dtype=torch.bfloat16, device=dev)
+        pag = (w, copies, S, part, out, int(copies[0][4].sum()))
     torch.cuda.synchronize()
 
     def prefill_step(i, ev=None):
@@ -208,6 +231,18 @@ def main() -> int:
         if ev is not None:
             ev[0].record(stream)
         A.decode_splitk(q, kc, vc, lens, S, w.scale, partials=part)
+        if ev is not None:
+            ev[1].record(stream)
+        A.merge_partials(*part, torch.bfloat16, out=out)
+        if ev is not None:
+            ev[2].record(stream)
+
+    def paged_step(i, ev=None):
+        w, copies, S, part, out, _ = pag
+        q, kp, vp, table, lens = copies[i % 2]
+        if ev is not None:
+            ev[0].record(stream)
+        A.decode_splitk_paged(q, kp, vp, table, lens, S, w.scale, partials=part)
         if ev is not None:
             ev[1].record(stream)
         A.merge_partials(*part, torch.bfloat16, out=out)
@@ -276,7 +311,35 @@ def main() -> int:
             "traffic": measured_traffic("merge_partials_kernel<bf16,d128>", "merge_partials_kernel"),
             "algorithmic_bytes": part_bytes / 2})
 
-    dominant = max(result_kernels, key=lambda r: r["avg_ms"])
+    # ---- paged decode region (reported beside the step)
+    paged_line = None
+    if pag:
+        w, copies, S, part, out, total_len = pag
+        for i in range(W):
+            paged_step(i)
+        torch.cuda.synchronize()
+        ev = [events(3) for _ in range(K)]
+        t0 = time.perf_counter()
+        for i in range(K):
+            paged_step(i, ev[i])
+        torch.cuda.synchronize()
+        pag_wall = time.perf_counter() - t0
+        if not torch.isfinite(out).all():
+            raise RuntimeError("non-finite paged decode output")
+        kv_bytes = w.kv_bytes(total_len)
+        ms_split = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+        gbs = kv_bytes / (ms_split * 1e-3) / 1e9
+        label = f"decode_splitk_kernel<bf16,d128,paged{PAGE_SIZE}>"
+        result_kernels.append({
+            "kernel": label, "workload": f"{w.name} in {PAGE_SIZE}-row pages", "avg_ms": ms_split,
+            "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+            "traffic": measured_traffic(label, "decode_splitk_kernel"), "algorithmic_bytes": kv_bytes,
+            "num_splits": S, "in_step": False})
+        paged_line = {"value": kv_bytes * K / pag_wall / 1e9, "unit": "GB/s",
+                      "frac_of_hbm_peak": kv_bytes * K / pag_wall / 1e9 / PEAK_HBM_GBS, "page_size": PAGE_SIZE,
+                      "timed": "attn_decode_splitk_paged + attn_merge_partials, wall clock, outside the step"}
+
+    dominant = max([r for r in result_kernels if r.get("in_step", True)] or result_kernels, key=lambda r: r["avg_ms"])
     roofline = {k: dominant[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
     roofline["kernel"] = dominant["kernel"]
 
@@ -305,6 +368,7 @@ def main() -> int:
         "decode": ({"value": dec[0].kv_bytes(dec[5]) * K / dec_wall / 1e9, "unit": "GB/s",
                     "frac_of_hbm_peak": dec[0].kv_bytes(dec[5]) * K / dec_wall / 1e9 / PEAK_HBM_GBS,
                     "timed": "attn_decode_splitk + attn_merge_partials, wall clock"} if dec else None),
+        "decode_paged": paged_line,
         "roofline": roofline,
         "kernels": result_kernels,
     }

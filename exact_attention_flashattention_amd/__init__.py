@@ -9,8 +9,10 @@ Entry points (same names as the C ABI):
 
 * ``prefill_fwd(q, k, v, causal, scale)`` -- ``attn_prefill_fwd``
 * ``decode_splitk(q, k_cache, v_cache, kv_lens, num_splits, scale)`` -- ``attn_decode_splitk``
+* ``decode_splitk_paged(q, k_pages, v_pages, block_table, kv_lens, num_splits, scale)`` --
+  ``attn_decode_splitk_paged``
 * ``merge_partials(part_m, part_l, part_o, out_dtype)`` -- ``attn_merge_partials``
-* ``decode(...)`` -- the two decode calls back to back on one stream
+* ``decode(...)``, ``decode_paged(...)`` -- split-K then merge, back to back on one stream
 * ``decode_num_splits``, ``decode_chunk_len``, ``decode_workspace_bytes`` -- host helpers
 """
 
@@ -24,8 +26,8 @@ import torch
 from . import _lib
 from ._lib import ATTN_BF16, ATTN_F16, AttnError  # noqa: F401
 
-__all__ = ["prefill_fwd", "decode_splitk", "merge_partials", "decode", "decode_num_splits", "decode_chunk_len",
-           "decode_workspace_bytes", "AttnError"]
+__all__ = ["prefill_fwd", "decode_splitk", "decode_splitk_paged", "merge_partials", "decode", "decode_paged",
+           "decode_num_splits", "decode_chunk_len", "decode_workspace_bytes", "AttnError"]
 
 _DTYPES = {torch.bfloat16: ATTN_BF16, torch.float16: ATTN_F16}
 
@@ -111,6 +113,38 @@ def decode_splitk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     return pm, pl, po
 
 
+def decode_splitk_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, block_table: torch.Tensor,
+                        kv_lens: torch.Tensor, num_splits: Optional[int] = None, scale: Optional[float] = None,
+                        partials=None):
+    """Partial states over a paged cache: ``k_pages, v_pages: [P, Hkv, page, d]``,
+    ``block_table: [B, max_pages]`` int32 (device).  Same outputs as ``decode_splitk``."""
+    lib = _lib_handle()
+    if q.dim() != 3 or k_pages.dim() != 4 or v_pages.shape != k_pages.shape or block_table.dim() != 2:
+        raise ValueError("expected q [B, Hq, d], pages [P, Hkv, page, d] and block_table [B, max_pages]")
+    B, hq, d = q.shape
+    P, hkv, page, dk = k_pages.shape
+    if dk != d or k_pages.dtype != q.dtype or v_pages.dtype != q.dtype:
+        raise ValueError("q and pages disagree in head dim or dtype")
+    if block_table.dtype != torch.int32 or block_table.shape[0] != B or block_table.device != q.device:
+        raise ValueError("block_table must be an int32 device tensor [B, max_pages]")
+    if kv_lens.dtype != torch.int32 or kv_lens.numel() != B or kv_lens.device != q.device:
+        raise ValueError("kv_lens must be an int32 device tensor with one entry per sequence")
+    max_pages = block_table.shape[1]
+    S = decode_num_splits(B, hkv, max_pages * page) if num_splits is None else int(num_splits)
+    if partials is None:
+        pm = torch.empty((B, hq, S), dtype=torch.float32, device=q.device)
+        pl = torch.empty((B, hq, S), dtype=torch.float32, device=q.device)
+        po = torch.empty((B, hq, S, d), dtype=torch.float32, device=q.device)
+    else:
+        pm, pl, po = partials
+    st = lib.attn_decode_splitk_paged(_dev(q, "q"), _dev(k_pages, "k_pages"), _dev(v_pages, "v_pages"),
+                                      _dev(block_table, "block_table"), max_pages, P, page,
+                                      _dev(kv_lens, "kv_lens"), _dtype_code(q), B, hq, hkv, d, _scale(scale, d), S,
+                                      _dev(pm, "part_m"), _dev(pl, "part_l"), _dev(po, "part_o"), _stream(q))
+    _lib.check("attn_decode_splitk_paged", st)
+    return pm, pl, po
+
+
 def merge_partials(part_m: torch.Tensor, part_l: torch.Tensor, part_o: torch.Tensor,
                    out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Merge ``[B, Hq, S]`` / ``[B, Hq, S, d]`` fp32 partials into ``[B, Hq, d]`` of ``out_dtype``."""
@@ -132,4 +166,12 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_len
            num_splits: Optional[int] = None, scale: Optional[float] = None, partials=None) -> torch.Tensor:
     """Single-query decode: split-K partials then their merge, on the current stream."""
     pm, pl, po = decode_splitk(q, k_cache, v_cache, kv_lens, num_splits, scale, partials)
+    return merge_partials(pm, pl, po, q.dtype)
+
+
+def decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, block_table: torch.Tensor,
+                 kv_lens: torch.Tensor, num_splits: Optional[int] = None, scale: Optional[float] = None,
+                 partials=None) -> torch.Tensor:
+    """Single-query decode over a paged cache: paged split-K partials then their merge."""
+    pm, pl, po = decode_splitk_paged(q, k_pages, v_pages, block_table, kv_lens, num_splits, scale, partials)
     return merge_partials(pm, pl, po, q.dtype)

@@ -24,6 +24,17 @@
 //
 // The kernel is bound by HBM reads of K and V; the matrix cores and the
 // softmax arithmetic are far below their limits at g <= 16.
+//
+// Paged caches ("PagedAttention's kernel difference" in section 5 of
+// "Attention Computation in Practice"): the same kernel with PAGED = true
+// reads logical cache row j of sequence b from page block_table[b][j / P] at
+// row j % P, the pool laid out [num_pages, hkv, P, d].  P is a power of two
+// >= 16 and every split starts on a multiple of 64, so each 16-row half of a
+// 32-key step lies inside one page: a step gathers through two buffer
+// resources per tensor instead of one.  The page ids of the split's next 64
+// pages sit one per lane in a VGPR (one vector load, refreshed when a split
+// runs past them) and are picked out with v_readlane, so the gather adds no
+// memory round trip to a step.
 #include "device_common.hpp"
 #include "launchers.hpp"
 
@@ -43,11 +54,19 @@ struct DecodeStage {
 
 }  // namespace
 
-template <class T, int D>
+// Where a paged kernel finds its pages (unused by the contiguous kernel).
+struct PageTable {
+  const int* table;  // [batch, max_pages] page ids
+  int max_pages;     // table row length
+  int num_pages;     // pages in the pool; ids are clamped into [0, num_pages)
+  int shift;         // log2 of the page size
+};
+
+template <class T, int D, bool PAGED>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void decode_splitk_kernel(
     const char* __restrict__ q, const char* __restrict__ kc, const char* __restrict__ vc,
     const int* __restrict__ kv_lens, int max_kv_len, int hq, int hkv, int g, int chunk, int num_splits, float c,
-    float* __restrict__ part_m, float* __restrict__ part_l, float* __restrict__ part_o) {
+    float* __restrict__ part_m, float* __restrict__ part_l, float* __restrict__ part_o, PageTable pt) {
   constexpr int KK = D / 32;
   constexpr int DT = D / 16;              // 16-row output tiles of the head dimension
   constexpr int VCH = D / 16;
@@ -111,16 +130,57 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     const int cidx = lane + 64 * i;
     v_off[i] = (uint32_t)(cidx / CPR) * D * 2 + (cidx % CPR) * 16;
   }
+  // paged: ids of pages [tab_base, tab_base + 64) of this sequence, lane i
+  // holding page tab_base + i (entries past the table row read as 0)
+  int tab = 0, tab_base = 0;
+  auto fetch_table = [&](int p0) {
+    tab_base = p0;
+    const int p = p0 + lane;
+    tab = p < pt.max_pages ? pt.table[(size_t)b * pt.max_pages + p] : 0;
+  };
+  if constexpr (PAGED) fetch_table(start >> pt.shift);
+  // byte offset in the pool of logical row `key` (a multiple of 16) of KV head kh
+  auto paged_row = [&](int key) -> size_t {
+    const int p = key >> pt.shift;
+    if (p - tab_base >= 64) fetch_table(p);
+    int id = __builtin_amdgcn_readlane(tab, p - tab_base);
+    id = id < 0 ? 0 : (id >= pt.num_pages ? pt.num_pages - 1 : id);
+    return ((((size_t)id * hkv + kh) << pt.shift) + (key & ((1 << pt.shift) - 1))) * (size_t)(D * 2);
+  };
+
   auto load = [&](DecodeStage<D>& st, int k0) {
-    const uint32_t bytes = (uint32_t)(end - k0) * D * 2;
-    const bufres rk = make_bufres(kbase + (size_t)k0 * D * 2, bytes);
-    const bufres rv = make_bufres(vbase + (size_t)k0 * D * 2, bytes);
+    if constexpr (PAGED) {
+      // rows [k0 + 16·sb, +16) of each half lie in one page
+      constexpr int VHALF = VCH / 2;  // V chunks per 16-row half
+      bufres rk[2], rv[2];
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
+      for (int sb = 0; sb < 2; ++sb) {
+        const int kr = k0 + 16 * sb;
+        // (readfirstlane: the clamp may be computed with a vector min/max, and a
+        // resource in vector registers would make every load a waterfall loop)
+        const int rows = __builtin_amdgcn_readfirstlane(end - kr < 0 ? 0 : (end - kr > 16 ? 16 : end - kr));
+        const size_t off = rows > 0 ? paged_row(kr) : 0;
+        rk[sb] = make_bufres(kc + off, (uint32_t)rows * D * 2);
+        rv[sb] = make_bufres(vc + off, (uint32_t)rows * D * 2);
+      }
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) st.k[sb][kk] = bload16(rk, k_off[sb][kk]);
+      for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-    for (int i = 0; i < VCH; ++i) st.v[i] = bload16(rv, v_off[i]);
+        for (int kk = 0; kk < KK; ++kk) st.k[sb][kk] = bload16(rk[sb], k_off[0][kk]);
+#pragma unroll
+      for (int i = 0; i < VCH; ++i)
+        st.v[i] = bload16(rv[i / VHALF], v_off[i] - (uint32_t)(i / VHALF) * 16 * D * 2);
+    } else {
+      const uint32_t bytes = (uint32_t)(end - k0) * D * 2;
+      const bufres rk = make_bufres(kbase + (size_t)k0 * D * 2, bytes);
+      const bufres rv = make_bufres(vbase + (size_t)k0 * D * 2, bytes);
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) st.k[sb][kk] = bload16(rk, k_off[sb][kk]);
+#pragma unroll
+      for (int i = 0; i < VCH; ++i) st.v[i] = bload16(rv, v_off[i]);
+    }
   };
 
   float m_run = kNegInf, l_run = 0.f;
@@ -206,33 +266,52 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   }
 }
 
-template <class T, int D>
+template <class T, int D, bool PAGED>
 static hipError_t launch_decode_t(const void* q, const void* kc, const void* vc, const int* kv_lens, int max_kv_len,
                                   int batch, int hq, int hkv, float scale, int num_splits, int chunk, float* pm,
-                                  float* pl, float* po, hipStream_t stream) {
+                                  float* pl, float* po, PageTable pt, hipStream_t stream) {
   const int g = hq / hkv;
   const int groups = (g + 15) / 16;
   dim3 grid(num_splits, hkv * groups, batch);
-  decode_splitk_kernel<T, D><<<grid, dim3(64), 0, stream>>>(
+  decode_splitk_kernel<T, D, PAGED><<<grid, dim3(64), 0, stream>>>(
       static_cast<const char*>(q), static_cast<const char*>(kc), static_cast<const char*>(vc), kv_lens, max_kv_len,
-      hq, hkv, g, chunk, num_splits, scale * kLog2e, pm, pl, po);
+      hq, hkv, g, chunk, num_splits, scale * kLog2e, pm, pl, po, pt);
   return hipGetLastError();
+}
+
+template <bool PAGED>
+static hipError_t launch_decode_any(const void* q, const void* kc, const void* vc, const int* kv_lens,
+                                    int max_kv_len, bool bf16, int batch, int hq, int hkv, int d, float scale,
+                                    int num_splits, int chunk, float* pm, float* pl, float* po, PageTable pt,
+                                    hipStream_t stream) {
+  if (bf16) {
+    return d == 64 ? launch_decode_t<Bf16, 64, PAGED>(q, kc, vc, kv_lens, max_kv_len, batch, hq, hkv, scale,
+                                                      num_splits, chunk, pm, pl, po, pt, stream)
+                   : launch_decode_t<Bf16, 128, PAGED>(q, kc, vc, kv_lens, max_kv_len, batch, hq, hkv, scale,
+                                                       num_splits, chunk, pm, pl, po, pt, stream);
+  }
+  return d == 64 ? launch_decode_t<F16, 64, PAGED>(q, kc, vc, kv_lens, max_kv_len, batch, hq, hkv, scale,
+                                                   num_splits, chunk, pm, pl, po, pt, stream)
+                 : launch_decode_t<F16, 128, PAGED>(q, kc, vc, kv_lens, max_kv_len, batch, hq, hkv, scale,
+                                                    num_splits, chunk, pm, pl, po, pt, stream);
 }
 
 hipError_t launch_decode_splitk(const void* q, const void* k_cache, const void* v_cache, const int* kv_lens,
                                 int max_kv_len, bool bf16, int batch, int hq, int hkv, int d, float scale,
                                 int num_splits, int chunk, float* part_m, float* part_l, float* part_o,
                                 hipStream_t stream) {
-  if (bf16) {
-    return d == 64 ? launch_decode_t<Bf16, 64>(q, k_cache, v_cache, kv_lens, max_kv_len, batch, hq, hkv, scale,
-                                               num_splits, chunk, part_m, part_l, part_o, stream)
-                   : launch_decode_t<Bf16, 128>(q, k_cache, v_cache, kv_lens, max_kv_len, batch, hq, hkv, scale,
-                                                num_splits, chunk, part_m, part_l, part_o, stream);
-  }
-  return d == 64 ? launch_decode_t<F16, 64>(q, k_cache, v_cache, kv_lens, max_kv_len, batch, hq, hkv, scale,
-                                            num_splits, chunk, part_m, part_l, part_o, stream)
-                 : launch_decode_t<F16, 128>(q, k_cache, v_cache, kv_lens, max_kv_len, batch, hq, hkv, scale,
-                                             num_splits, chunk, part_m, part_l, part_o, stream);
+  return launch_decode_any<false>(q, k_cache, v_cache, kv_lens, max_kv_len, bf16, batch, hq, hkv, d, scale,
+                                  num_splits, chunk, part_m, part_l, part_o, PageTable{nullptr, 0, 0, 0}, stream);
+}
+
+hipError_t launch_decode_splitk_paged(const void* q, const void* k_pages, const void* v_pages,
+                                      const int* block_table, int max_pages, int num_pages, int page_shift,
+                                      const int* kv_lens, bool bf16, int batch, int hq, int hkv, int d, float scale,
+                                      int num_splits, int chunk, float* part_m, float* part_l, float* part_o,
+                                      hipStream_t stream) {
+  return launch_decode_any<true>(q, k_pages, v_pages, kv_lens, max_pages << page_shift, bf16, batch, hq, hkv, d,
+                                 scale, num_splits, chunk, part_m, part_l, part_o,
+                                 PageTable{block_table, max_pages, num_pages, page_shift}, stream);
 }
 
 }  // namespace attn

@@ -56,8 +56,7 @@ namespace {
 
 // Largest probability (as a power of two) used without raising the reference
 // maximum, and the matching bound on a lane's 16-key probability sum.
-constexpr float kRescaleLog2 = 8.f;
-constexpr float kRescaleSum = 256.f;  // 2^kRescaleLog2
+constexpr float kRescaleSum = 256.f;  // 2^8
 
 // NB 32-row query blocks per wave: two at d=64; one at d=128, where two
 // blocks' accumulators and Q operands would not fit two waves per SIMD.
@@ -374,9 +373,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // current reference m_run (the largest row maximum seen when it was last
   // raised).  The reference is raised -- to the row maximum so far, with l and
   // o rescaled by exp2(m_run - m_new) -- and the subtile recomputed only when
-  // some lane's 16 probabilities sum past 2^kRescaleLog2, or on a row's first
+  // some lane's 16 probabilities sum past 2^8, or on a row's first
   // subtile (no reference yet).  Every probability used is therefore at most
-  // 2^kRescaleLog2 and the row maximum is at most kRescaleLog2 above the
+  // 2^8 and the row maximum is at most 8 above the
   // reference, so nothing overflows or loses precision; o and l share the
   // reference, so o/l is the same either way.
   float neg_ref[NB], lim[NB];  // -m_run (0 while m_run = -inf); the row-sum limit (-1 forces a raise)

@@ -134,6 +134,40 @@ attn_status attn_decode_splitk(const void* q, const void* k_cache, const void* v
                                int num_splits, float* part_m, float* part_l, float* part_o, void* stream);
 
 /*
+ * attn_decode_splitk_paged -- attn_decode_splitk over a paged KV cache.
+ *
+ * The cache is a pool of fixed-size pages; each sequence lists its pages in a
+ * block table, and the kernel gathers through it ("PagedAttention's kernel
+ * difference" in section 5 of "Attention Computation in Practice").  Logical
+ * cache row j of sequence b is row j % page_size of page
+ * block_table[b·max_pages_per_seq + j / page_size].  Partials, splits and
+ * units are exactly those of attn_decode_splitk with
+ * max_kv_len = max_pages_per_seq · page_size, so the same merge applies and,
+ * for the same logical cache contents, the partials are bit-identical.
+ *
+ *   q           : [batch, hq, d]                        elements of `dtype`
+ *   k_pages     : [num_pages, hkv, page_size, d]        elements of `dtype`
+ *   v_pages     : [num_pages, hkv, page_size, d]        elements of `dtype`
+ *   block_table : [batch, max_pages_per_seq] int32, DEVICE memory.  Only the
+ *                 first ceil(kv_lens[b] / page_size) entries of row b are
+ *                 used; each must lie in [0, num_pages) (out-of-range ids are
+ *                 clamped into that range, so no read leaves the pool).
+ *                 Pages may be shared between sequences.
+ *   kv_lens     : [batch] int32, DEVICE memory; sequence b sees logical rows
+ *                 0 .. kv_lens[b]-1, clamped into [0, max_pages_per_seq ·
+ *                 page_size]; rows at or past it are never read.
+ *   page_size   : a power of two >= 16 (else ATTN_ERR_UNSUPPORTED)
+ *   part_m, part_l, part_o, num_splits : as for attn_decode_splitk
+ *
+ * Limits: max_pages_per_seq · page_size below 2^31 / d;
+ * num_pages·hkv·page_size·d below 2^40 (else ATTN_ERR_TOO_LARGE).
+ */
+attn_status attn_decode_splitk_paged(const void* q, const void* k_pages, const void* v_pages,
+                                     const int* block_table, int max_pages_per_seq, int num_pages, int page_size,
+                                     const int* kv_lens, int dtype, int batch, int hq, int hkv, int d, float scale,
+                                     int num_splits, float* part_m, float* part_l, float* part_o, void* stream);
+
+/*
  * attn_merge_partials -- merge the partial states of each (sequence, head)
  * and normalise: m = max_s m_s, l = sum_s l_s·exp(m_s − m),
  * o = sum_s o_s·exp(m_s − m), O = o / l (the two-state merge rule of "Maths"

@@ -15,6 +15,8 @@ from .attention import (  # noqa: F401
     attention,
     attention_rows,
     decode,
+    decode_paged,
+    gather_pages,
     merge_pair,
     merge_partials,
     online_softmax_tiled,

@@ -21,6 +21,10 @@ What it computes, with where each step is defined:
 * Decode: one query per sequence sees keys ``0 .. kv_len-1`` of its cache and
   nothing past them ("Prefill and decode are different problems" on the first
   page; "Concept" on "Attention kernels").
+* Paged decode: the same, with cache row ``j`` read from page
+  ``block_table[b][j // page_size]`` at row ``j % page_size``
+  ("PagedAttention's kernel difference", section 5 of "Attention Computation
+  in Practice").
 * A partial state ``(m, l, o)`` over a set of keys is the running maximum, the
   sum of ``exp(s_j - m)`` and the unnormalised ``sum_j exp(s_j - m) v_j``;
   two states merge by ``m = max(m_a, m_b)``, ``l = l_a e^(m_a-m) + l_b e^(m_b-m)``,
@@ -153,6 +157,55 @@ def decode(q, k_cache, v_cache, kv_lens, scale: float):
         for kh in range(Hkv):
             K = _f64(k_cache[b, kh, :L])
             V = _f64(v_cache[b, kh, :L])
+            out[b, kh * g:(kh + 1) * g] = _materialised_rows(q[b, kh * g:(kh + 1) * g], K, V, scale)
+    return out
+
+
+def gather_pages(pages, table_row, length: int, kv_head: int):
+    """Logical cache rows ``0 .. length-1`` of one KV head of one sequence,
+    read out of a paged pool.
+
+    ``pages: [P, Hkv, page_size, d]``; ``table_row`` lists the sequence's
+    pages in order.  Row ``j`` is row ``j % page_size`` of page
+    ``table_row[j // page_size]`` ("PagedAttention's kernel difference",
+    section 5 of "Attention Computation in Practice": the kernel reads block
+    after block through the block table).  Entries of the table past the
+    pages the length needs are not looked at.
+    """
+    pages = np.asarray(pages)
+    ps = pages.shape[2]
+    rows = np.empty((length, pages.shape[3]), dtype=pages.dtype)
+    for j in range(length):
+        page = int(table_row[j // ps])
+        if not 0 <= page < pages.shape[0]:
+            raise ValueError(f"block table names page {page}; the pool holds {pages.shape[0]}")
+        rows[j] = pages[page, kv_head, j % ps]
+    return rows
+
+
+def decode_paged(q, k_pages, v_pages, block_table, kv_lens, scale: float):
+    """Single-query attention over a paged KV cache.
+
+    ``q: [B, Hq, d]``, ``k_pages, v_pages: [P, Hkv, page_size, d]``,
+    ``block_table: [B, max_pages]``, ``kv_lens: [B]``.  The gather of
+    ``gather_pages`` followed by the same attention as ``decode``: the pages
+    change where rows live, not what is computed.  Returns ``O: [B, Hq, d]``
+    in fp64.
+    """
+    q = _f64(q)
+    B, Hq, d = q.shape
+    Hkv = k_pages.shape[1]
+    g = Hq // Hkv
+    kv_head_of(0, Hq, Hkv)
+    capacity = block_table.shape[1] * k_pages.shape[2]
+    out = np.zeros((B, Hq, d))
+    for b in range(B):
+        L = int(kv_lens[b])
+        if not 0 <= L <= capacity:
+            raise ValueError(f"kv_lens[{b}]={L} outside [0, {capacity}]")
+        for kh in range(Hkv):
+            K = _f64(gather_pages(k_pages, block_table[b], L, kh))
+            V = _f64(gather_pages(v_pages, block_table[b], L, kh))
             out[b, kh * g:(kh + 1) * g] = _materialised_rows(q[b, kh * g:(kh + 1) * g], K, V, scale)
     return out
 

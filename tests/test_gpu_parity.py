@@ -244,6 +244,116 @@ def test_decode_ragged_full_sampled(A):
         assert_close(out[b], ref, f"{RAG.name} b={b} L={L}")
 
 
+# --- paged decode ----------------------------------------------------------------------
+
+def paged_case(A, w, kv_lens, max_len, batch, page_size, num_splits, seed=0, spare=5):
+    """Paged split-K + merge against the oracle's gather-then-attend, and the
+    paged partials against the contiguous kernel's on the same logical cache
+    (bit-identical when both see the same split length)."""
+    announce(f"paged {w.name} B={batch} L={max_len} page={page_size} lens={kv_lens.tolist()[:6]} S={num_splits}")
+    q, kc, vc, lens = workloads.decode_inputs(w, device=DEV, salt=seed, kv_lens=kv_lens, max_kv_len=max_len,
+                                              batch=batch)
+    kp, vp, table = workloads.paged_from_cache(kc, vc, lens, page_size, workloads.seed_for(w.name, "pages", seed),
+                                               spare_pages=spare)
+    lens_d, table_d = lens.to(DEV), table.to(DEV)
+    capacity = table.shape[1] * page_size
+    S = A.decode_num_splits(batch, w.hkv, capacity) if num_splits is None else num_splits
+    pm, pl, po = A.decode_splitk_paged(q, kp, vp, table_d, lens_d, S, w.scale)
+    out = A.merge_partials(pm, pl, po, q.dtype)
+    cm, cl, co = A.decode_splitk(q, kc, vc, lens_d, S, w.scale)
+    torch.cuda.synchronize()
+    if A.decode_chunk_len(capacity, S) == A.decode_chunk_len(max_len, S):
+        assert torch.equal(pm, cm) and torch.equal(pl, cl) and torch.equal(po, co), "paged != contiguous partials"
+    ref = oracle.decode_paged(f64(q), f64(kp), f64(vp), table.numpy(), lens.numpy(), w.scale)
+    assert_close(out, ref, f"paged {w.name} page={page_size} S={S}")
+    return q, kp, vp, table, lens, out
+
+
+@pytest.mark.parametrize("page_size", [16, 32, 64, 256])
+@pytest.mark.parametrize("S", [None, 3])
+def test_decode_paged_lengths_and_page_sizes(A, page_size, S):
+    """Lengths 0, 1, 15-17 (page edges), a split edge and the full capacity."""
+    lens = torch.tensor([0, 1, 15, 16, 17, 700, 1024, 1100, 2048], dtype=torch.int32)
+    paged_case(A, DEC, lens, 2048, len(lens), page_size, S)
+
+
+@pytest.mark.parametrize("S", [1, 2])
+def test_decode_paged_split_longer_than_64_pages(A, S):
+    """Splits of 1536 and 3072 keys span more than 64 pages of 16 rows, so the
+    kernel reloads its per-lane copy of the block table inside a split."""
+    lens = torch.tensor([3072, 2500, 1025], dtype=torch.int32)
+    paged_case(A, DEC, lens, 3072, 3, 16, S)
+
+
+@pytest.mark.parametrize("hq,hkv,d,dtype,page_size", [(4, 4, 128, "bf16", 16), (16, 1, 64, "bf16", 32),
+                                                      (24, 1, 128, "f16", 16), (32, 2, 64, "f16", 64),
+                                                      (64, 8, 128, "bf16", 128)])
+def test_decode_paged_head_layouts(A, hq, hkv, d, dtype, page_size):
+    w = workloads.Decode(f"decode_paged_case_{hq}_{hkv}_{d}_{dtype}", 3, hq, hkv, d, 768, None, 1.0, dtype)
+    paged_case(A, w, torch.tensor([768, 333, 64], dtype=torch.int32), 768, 3, page_size, None)
+
+
+def test_decode_paged_shared_pages(A):
+    """Two sequences listing the same pages (a shared prefix) with equal queries
+    give equal outputs; a third shares the first 4 pages and then diverges."""
+    announce("paged shared pages")
+    w = DEC
+    hq, hkv, d, ps = w.hq, w.hkv, w.d, 16
+    kp = workloads.normal((12, hkv, ps, d), "bf16", workloads.seed_for("paged_shared", "k"), DEV)
+    vp = workloads.normal((12, hkv, ps, d), "bf16", workloads.seed_for("paged_shared", "v"), DEV)
+    q1 = workloads.normal((1, hq, d), "bf16", workloads.seed_for("paged_shared", "q"), DEV)
+    q = q1.repeat(3, 1, 1).contiguous()
+    table = torch.tensor([[7, 2, 9, 4, 11, 0], [7, 2, 9, 4, 11, 0], [7, 2, 9, 4, 1, 3]], dtype=torch.int32)
+    lens = torch.tensor([90, 90, 96], dtype=torch.int32)
+    out = A.decode_paged(q, kp, vp, table.to(DEV), lens.to(DEV), None, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out[0], out[1])
+    ref = oracle.decode_paged(f64(q), f64(kp), f64(vp), table.numpy(), lens.numpy(), w.scale)
+    assert_close(out, ref, "paged shared pages")
+
+
+def test_decode_paged_clamps_out_of_range_page_ids(A):
+    """A page id below 0 reads page 0 and one past the pool reads the last page,
+    so a bad table never reads outside the pool."""
+    announce("paged clamp")
+    w = DEC
+    q, kc, vc, lens = workloads.decode_inputs(w, device=DEV, max_kv_len=64, batch=1)
+    kp, vp, table = workloads.paged_from_cache(kc, vc, lens, 16, 11, spare_pages=0)
+    P = kp.shape[0]
+    bad = table.clone()
+    bad[0, 1], bad[0, 3] = -7, P + 100
+    out = A.decode_paged(q, kp, vp, bad.to(DEV), lens.to(DEV), None, w.scale)
+    torch.cuda.synchronize()
+    fixed = bad.clone()
+    fixed[0, 1], fixed[0, 3] = 0, P - 1
+    ref = oracle.decode_paged(f64(q), f64(kp), f64(vp), fixed.numpy(), lens.numpy(), w.scale)
+    assert_close(out, ref, "paged clamp")
+
+
+def test_decode_paged_long_context_full(A):
+    """The 262144-key, 32/8-head cache as 16384 scattered 16-row pages (the
+    benchmarked paged launch): partials bit-identical to the contiguous kernel's,
+    whole output against the oracle."""
+    announce(f"paged {DEC.name}")
+    q, kc, vc, lens = workloads.decode_inputs(DEC, device=DEV)
+    kp, vp, table = workloads.paged_from_cache(kc, vc, lens, 16, workloads.seed_for(DEC.name, "pages"))
+    lens_d, table_d = lens.to(DEV), table.to(DEV)
+    S = A.decode_num_splits(1, DEC.hkv, DEC.max_kv_len)
+    pm, pl, po = A.decode_splitk_paged(q, kp, vp, table_d, lens_d, S, DEC.scale)
+    cm, cl, co = A.decode_splitk(q, kc, vc, lens_d, S, DEC.scale)
+    out = A.merge_partials(pm, pl, po, q.dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(pm, cm) and torch.equal(pl, cl) and torch.equal(po, co)
+    del kp, vp
+    g = DEC.hq // DEC.hkv
+    qf = f64(q)
+    ref = np.zeros((1, DEC.hq, DEC.d))
+    for kh in range(DEC.hkv):
+        K, V = f64(kc[0, kh]), f64(vc[0, kh])
+        ref[0, kh * g:(kh + 1) * g] = oracle.attention_rows(qf[0, kh * g:(kh + 1) * g], K, V, DEC.scale)
+    assert_close(out, ref, f"paged {DEC.name}")
+
+
 # --- merge -----------------------------------------------------------------------------
 
 @pytest.mark.parametrize("S", [1, 2, 9, 300])

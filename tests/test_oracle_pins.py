@@ -307,6 +307,85 @@ def test_decode_with_no_keys_is_zero():
     assert np.array_equal(out, np.zeros((1, 2, 8)))
 
 
+# --- paged decode ("PagedAttention's kernel difference", "Attention Computation in Practice" section 5) ---
+
+def test_gather_pages_reads_the_listed_blocks_in_order():
+    """Every pool element encodes (page, head, row); with table [2, 0, 3] and
+    page size 4, logical rows 0-3 come from page 2, rows 4-7 from page 0 and
+    rows 8-9 from page 3, in row order -- written out by hand below."""
+    P, H, ps, d = 4, 2, 4, 3
+    pool = np.zeros((P, H, ps, d))
+    for p_ in range(P):
+        for h in range(H):
+            for r in range(ps):
+                pool[p_, h, r] = 100 * p_ + 10 * h + r
+    got = oracle.gather_pages(pool, [2, 0, 3, 1], 10, 1)
+    want = [210, 211, 212, 213, 10, 11, 12, 13, 310, 311]
+    assert np.array_equal(got[:, 0], np.array(want, dtype=float))
+    assert np.array_equal(got, np.repeat(got[:, :1], d, axis=1))
+    assert oracle.gather_pages(pool, [2, 0, 3, 1], 0, 0).shape == (0, d)
+    with pytest.raises(ValueError):
+        oracle.gather_pages(pool, [2, 7], 8, 0)
+
+
+def contiguous_as_identity_pages(kc, ps):
+    """Pool in which sequence b's block i is page b·nblk + i (no permutation)."""
+    B, H, L, d = kc.shape
+    nblk = L // ps
+    pool = kc.reshape(B, H, nblk, ps, d).transpose(0, 2, 1, 3, 4).reshape(B * nblk, H, ps, d)
+    table = np.arange(B * nblk).reshape(B, nblk)
+    return pool, table
+
+
+@pytest.mark.parametrize("ps", [1, 4, 16])
+def test_paged_decode_with_identity_table_is_contiguous_decode_bit_exact(ps):
+    B, hq, hkv, L, d = 3, 8, 2, 48, 16
+    lens = [48, 1, 17]
+    q = gauss(70, B, hq, d)
+    kc, vc = gauss(71, B, hkv, L, d), gauss(72, B, hkv, L, d)
+    kp, table = contiguous_as_identity_pages(kc, ps)
+    vp, _ = contiguous_as_identity_pages(vc, ps)
+    assert np.array_equal(oracle.decode_paged(q, kp, vp, table, lens, 0.25), oracle.decode(q, kc, vc, lens, 0.25))
+
+
+def test_paged_decode_scattered_pages_match_sdpa_and_skip_unused_rows():
+    """Pages in a seeded random order, NaN in spare pages and in each
+    sequence's last-page tail: the output equals library attention over the
+    first kv_len rows."""
+    B, hq, hkv, L, d, ps = 3, 8, 2, 64, 16, 16
+    lens = torch.tensor([64, 1, 33], dtype=torch.int32)
+    q = gauss(73, B, hq, d)
+    kc, vc = gauss(74, B, hkv, L, d), gauss(75, B, hkv, L, d)
+    for b, n in enumerate(lens.tolist()):
+        kc[b, :, n:] = np.nan
+        vc[b, :, n:] = np.nan
+    kp, vp, table = workloads.paged_from_cache(torch.from_numpy(kc), torch.from_numpy(vc), lens, ps, seed=5,
+                                               spare_pages=3)
+    kp, vp, table = kp.numpy(), vp.numpy(), table.numpy()
+    assert sorted(table[table >= 0].tolist()) != list(range(int((table >= 0).sum())))  # really scattered
+    out = oracle.decode_paged(q, kp, vp, table, lens.numpy(), 0.25)
+    assert np.all(np.isfinite(out))
+    for b, n in enumerate(lens.tolist()):
+        tk = torch.from_numpy(kc[b, :, :n]).repeat_interleave(hq // hkv, dim=0)
+        tv = torch.from_numpy(vc[b, :, :n]).repeat_interleave(hq // hkv, dim=0)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[b])[:, None], tk, tv, scale=0.25)[:, 0]
+        assert np.max(np.abs(out[b] - ref.numpy())) <= TOL
+
+
+def test_paged_decode_shared_pages_give_equal_outputs():
+    """Two sequences whose tables list the same pages (a shared prefix) and
+    whose queries are equal produce equal outputs; a different length does not."""
+    hq, hkv, d, ps = 4, 1, 8, 4
+    pool_k, pool_v = gauss(76, 6, hkv, ps, d), gauss(77, 6, hkv, ps, d)
+    q1 = gauss(78, 1, hq, d)
+    q = np.concatenate([q1, q1, q1])
+    table = np.array([[5, 1, 3], [5, 1, 3], [5, 1, 0]])
+    out = oracle.decode_paged(q, pool_k, pool_v, table, [10, 10, 12], 0.5)
+    assert np.array_equal(out[0], out[1])
+    assert not np.array_equal(out[0], out[2])
+
+
 def test_attention_rows_matches_full_output():
     B, hq, n, d = 1, 2, 130, 32
     q, k, v = gauss(62, B, hq, n, d), gauss(63, B, hq, n, d), gauss(64, B, hq, n, d)

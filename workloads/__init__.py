@@ -166,6 +166,50 @@ def decode_inputs(w: Decode, device="cpu", salt: int = 0, kv_lens: Optional[torc
     return q, k, v, kv_lens
 
 
+def paged_from_cache(k_cache: torch.Tensor, v_cache: torch.Tensor, kv_lens: torch.Tensor, page_size: int,
+                     seed: int, spare_pages: int = 0):
+    """Lay a contiguous cache ``[B, Hkv, Lmax, d]`` out as a paged pool.
+
+    Sequence ``b`` gets ``ceil(kv_lens[b] / page_size)`` pages, taken from a
+    seeded random permutation of the pool so that consecutive blocks of a
+    sequence are scattered; ``spare_pages`` more pages belong to nobody.
+    Returns ``(k_pages, v_pages, block_table)``: pools
+    ``[P, Hkv, page_size, d]`` (NaN wherever no cache row was copied: spare
+    pages and the tail of each sequence's last page) and an int32 table
+    ``[B, ceil(Lmax / page_size)]`` holding -1 past each sequence's pages.
+    Only rows are moved; nothing is computed.
+    """
+    B, hkv, L, d = k_cache.shape
+    ps = page_size
+    max_pages = -(-L // ps)
+    lens = [int(x) for x in kv_lens.tolist()]
+    need = [-(-n // ps) for n in lens]
+    total = sum(need) + spare_pages
+    gen = torch.Generator()
+    gen.manual_seed(seed & ((1 << 63) - 1))
+    perm = torch.randperm(max(total, 1), generator=gen)
+    dev = k_cache.device
+    pools = []
+    table = torch.full((B, max_pages), -1, dtype=torch.int32)
+    for cache in (k_cache, v_cache):
+        pool = torch.full((max(total, 1), hkv, ps, d), float("nan"), dtype=cache.dtype, device=dev)
+        pos = 0
+        for b in range(B):
+            n = need[b]
+            if n == 0:
+                continue
+            ids = perm[pos:pos + n]
+            table[b, :n] = ids.to(torch.int32)
+            rows = cache[b, :, :min(n * ps, L)]
+            if rows.shape[1] < n * ps:
+                fill = torch.full((hkv, n * ps - rows.shape[1], d), float("nan"), dtype=cache.dtype, device=dev)
+                rows = torch.cat([rows, fill], dim=1)
+            pool[ids.to(dev)] = rows.reshape(hkv, n, ps, d).transpose(0, 1)
+            pos += n
+        pools.append(pool)
+    return pools[0], pools[1], table
+
+
 def pages_decode_kv_bytes(seq_len: int, batch: int, kv_heads: int, head_dim: int, layers: int,
                           bytes_per_value: int = 2) -> float:
     """KV bytes one decode step reads for a whole model: K and V, every layer,
