@@ -23,9 +23,11 @@ last-level cache.
 
 After the step, the same decode is timed once more over a paged copy of the
 cache (16-row pages in a seeded random order, ``attn_decode_splitk_paged`` then
-``attn_merge_partials``) in a region of its own; it is reported beside the
-step (``decode_paged``, and in ``kernels``) and is not part of ``value`` or
-``ms_per_step``.
+``attn_merge_partials``) in a region of its own, and so is a packed append
+batch (16 sequences of 256..2048 new queries on 0..16384 cached positions,
+causal, ``attn_prefill_varlen_fwd``).  Both are reported beside the step
+(``decode_paged``, ``append``, and in ``kernels``) and are not part of
+``value`` or ``ms_per_step``.
 
 ``cpu_baseline`` times the fp64 oracle on a bounded sample of the same prefill
 workload (whole heads until about ``--cpu-seconds`` have passed), on the host
@@ -54,6 +56,7 @@ PEAK_HBM_GBS = 8000.0            # MI355X HBM3E peak
 PREFILL = ["prefill_b4_h32_n4096_d64_bf16", "prefill_b4_h32_n4096_d128_bf16"]
 DECODE = "decode_b1_hq32_hkv8_d128_len262144_bf16"
 PAGE_SIZE = 16
+APPEND = "append_causal_b16_hq32_hkv8_d128_q256to2048_past0to16384_bf16"
 CSRC = os.path.join(ROOT, "exact_attention_flashattention_amd", "csrc")
 KERNEL_SOURCES = {
     "prefill_fwd_kernel": ["prefill_fwd.hip", "device_common.hpp"],
@@ -141,7 +144,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "prefill_d64", "prefill_d128", "decode", "decode_paged"], default="all",
+    ap.add_argument("--only", choices=["all", "prefill_d64", "prefill_d128", "decode", "decode_paged", "append"], default="all",
                     help="run only one kernel family (for profiler runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of the bench, run plain device copies of this many MiB (counter calibration)")
@@ -177,6 +180,7 @@ def main() -> int:
     run_prefill = [n for n in PREFILL if args.only in ("all", "prefill_d" + n.split("_d")[1].split("_")[0])]
     run_decode = args.only in ("all", "decode")
     run_paged = args.only in ("all", "decode_paged")
+    run_append = args.only in ("all", "append")
 
     # ---- inputs (two copies each), outputs and workspaces: all allocated before timing
     pre = []
@@ -214,6 +218,16 @@ def main() -> int:
                 torch.empty((w.batch, w.hq, S, w.d), dtype=torch.float32, device=dev))
         out = torch.empty((w.batch, w.hq, w.d), dtype=torch.bfloat16, device=dev)
         pag = (w, copies, S, part, out, int(copies[0][4].sum()))
+    app = None
+    if run_append:
+        w = workloads.WORKLOADS[APPEND]
+        nq, nk = w.lengths()
+        copies = []
+        for s in (0, 1):
+            q, k, v, cu_q, cu_k = workloads.varlen_inputs(w, device=dev, salt=s, nq=nq, nk=nk)
+            copies.append((q, k, v, cu_q.to(dev), cu_k.to(dev)))
+        outs = [torch.empty_like(c[0]) for c in copies]
+        app = (w, copies, outs, nq, nk)
     torch.cuda.synchronize()
 
     def prefill_step(i, ev=None):
@@ -248,6 +262,15 @@ def main() -> int:
         A.merge_partials(*part, torch.bfloat16, out=out)
         if ev is not None:
             ev[2].record(stream)
+
+    def append_step(i, ev=None):
+        w, copies, outs, nq, nk = app
+        q, k, v, cu_q, cu_k = copies[i % 2]
+        if ev is not None:
+            ev[0].record(stream)
+        A.prefill_varlen_fwd(q, k, v, cu_q, cu_k, max(nq), max(nk), causal=w.causal, scale=w.scale, out=outs[i % 2])
+        if ev is not None:
+            ev[1].record(stream)
 
     def events(n):
         return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
@@ -339,6 +362,35 @@ def main() -> int:
                       "frac_of_hbm_peak": kv_bytes * K / pag_wall / 1e9 / PEAK_HBM_GBS, "page_size": PAGE_SIZE,
                       "timed": "attn_decode_splitk_paged + attn_merge_partials, wall clock, outside the step"}
 
+    # ---- append (varlen prefill) region (reported beside the step)
+    append_line = None
+    if app:
+        w, copies, outs, nq, nk = app
+        for i in range(W):
+            append_step(i)
+        torch.cuda.synchronize()
+        ev = [events(2) for _ in range(K)]
+        t0 = time.perf_counter()
+        for i in range(K):
+            append_step(i, ev[i])
+        torch.cuda.synchronize()
+        app_wall = time.perf_counter() - t0
+        if not torch.isfinite(outs[0]).all():
+            raise RuntimeError("non-finite append output")
+        flops = w.flops(nq, nk)
+        ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+        tflops = flops / (ms * 1e-3) / 1e12
+        label = "prefill_fwd_kernel<bf16,d128,causal,varlen>"
+        result_kernels.append({
+            "kernel": label, "workload": w.name, "avg_ms": ms, "bound": "mfma", "achieved": tflops,
+            "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s", "frac": tflops / PEAK_MFMA_BF16_TFLOPS,
+            "traffic": measured_traffic(label, "prefill_fwd_kernel"), "algorithmic_flops": flops,
+            "in_step": False})
+        append_line = {"value": flops * K / app_wall / 1e12, "unit": "TFLOP/s",
+                       "frac_of_mfma_peak": flops * K / app_wall / 1e12 / PEAK_MFMA_BF16_TFLOPS,
+                       "queries": sum(nq), "keys": sum(nk),
+                       "timed": "attn_prefill_varlen_fwd, wall clock, outside the step"}
+
     dominant = max([r for r in result_kernels if r.get("in_step", True)] or result_kernels, key=lambda r: r["avg_ms"])
     roofline = {k: dominant[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
     roofline["kernel"] = dominant["kernel"]
@@ -369,6 +421,7 @@ def main() -> int:
                     "frac_of_hbm_peak": dec[0].kv_bytes(dec[5]) * K / dec_wall / 1e9 / PEAK_HBM_GBS,
                     "timed": "attn_decode_splitk + attn_merge_partials, wall clock"} if dec else None),
         "decode_paged": paged_line,
+        "append": append_line,
         "roofline": roofline,
         "kernels": result_kernels,
     }

@@ -8,6 +8,8 @@ into exceptions.  torch provides device memory and streams, nothing else.
 Entry points (same names as the C ABI):
 
 * ``prefill_fwd(q, k, v, causal, scale)`` -- ``attn_prefill_fwd``
+* ``prefill_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, causal, scale)`` --
+  ``attn_prefill_varlen_fwd``
 * ``decode_splitk(q, k_cache, v_cache, kv_lens, num_splits, scale)`` -- ``attn_decode_splitk``
 * ``decode_splitk_paged(q, k_pages, v_pages, block_table, kv_lens, num_splits, scale)`` --
   ``attn_decode_splitk_paged``
@@ -26,7 +28,7 @@ import torch
 from . import _lib
 from ._lib import ATTN_BF16, ATTN_F16, AttnError  # noqa: F401
 
-__all__ = ["prefill_fwd", "decode_splitk", "decode_splitk_paged", "merge_partials", "decode", "decode_paged",
+__all__ = ["prefill_fwd", "prefill_varlen_fwd", "decode_splitk", "decode_splitk_paged", "merge_partials", "decode", "decode_paged",
            "decode_num_splits", "decode_chunk_len", "decode_workspace_bytes", "AttnError"]
 
 _DTYPES = {torch.bfloat16: ATTN_BF16, torch.float16: ATTN_F16}
@@ -72,6 +74,35 @@ def prefill_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool 
     st = lib.attn_prefill_fwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), _dtype_code(q), B, hq,
                               k.shape[1], n, d, _scale(scale, d), int(bool(causal)), _stream(q))
     _lib.check("attn_prefill_fwd", st)
+    return out
+
+
+def prefill_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                       cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int, causal: bool = False,
+                       scale: Optional[float] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Packed variable-length prefill / append: ``q [total_q, Hq, d]``, ``k, v [total_k, Hkv, d]``,
+    ``cu_seqlens_*`` int32 device tensors of ``batch + 1`` offsets; returns ``[total_q, Hq, d]``.
+    Queries are bottom-right aligned: query i of a sequence sees keys j <= i + nk - nq when causal."""
+    lib = _lib_handle()
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape:
+        raise ValueError("expected q [total_q, Hq, d] and k, v [total_k, Hkv, d]")
+    total_q, hq, d = q.shape
+    total_k, hkv, dk = k.shape
+    if dk != d or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v disagree in head dim or dtype")
+    for name, cu in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if cu.dtype != torch.int32 or cu.dim() != 1 or cu.device != q.device:
+            raise ValueError(f"{name} must be a 1-D int32 device tensor")
+    if cu_seqlens_k.numel() != cu_seqlens_q.numel() or cu_seqlens_q.numel() < 2:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold batch + 1 >= 2 offsets")
+    if out is None:
+        out = torch.empty_like(q)
+    st = lib.attn_prefill_varlen_fwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
+                                     _dev(cu_seqlens_q, "cu_seqlens_q"), _dev(cu_seqlens_k, "cu_seqlens_k"), total_q,
+                                     total_k, int(max_seqlen_q), int(max_seqlen_k), _dtype_code(q),
+                                     cu_seqlens_q.numel() - 1, hq, hkv, d, _scale(scale, d), int(bool(causal)),
+                                     _stream(q))
+    _lib.check("attn_prefill_varlen_fwd", st)
     return out
 
 

@@ -45,6 +45,17 @@
 //     sequence end (block classification of "Masking variants", "Attention
 //     Computation in Practice" section 5), and the longest query tiles are
 //     launched first.
+//
+// Variable-length batches (VARLEN = true; the append / mixed kernel of "The
+// four attention kernels you actually use", same section): sequences are
+// packed token-major, Q and O [total_q, hq, d], K and V [total_k, hkv, d], and
+// sequence b owns query rows cu_q[b] .. cu_q[b+1]-1 and key rows
+// cu_k[b] .. cu_k[b+1]-1.  Its nq queries are the LAST nq of its nk positions
+// (bottom-right alignment), so under the causal mask query i sees keys
+// j <= i + nk - nq; a square problem is the case nq = nk.  The only changes
+// are the row strides (a runtime value instead of the row size), the
+// per-sequence bases and lengths, and workgroups past a sequence's last query
+// tile returning at once.
 #include "device_common.hpp"
 #include "launchers.hpp"
 
@@ -130,10 +141,19 @@ __device__ __forceinline__ void pin(V& x) {
 
 }  // namespace
 
-template <class T, int D, bool CAUSAL>
+// Sequence bounds of a variable-length batch (unused by the square kernel).
+struct VarlenArgs {
+  const int* cu_q;  // [batch + 1] query row offsets
+  const int* cu_k;  // [batch + 1] key row offsets
+  int total_q;      // rows of Q / O; every sequence is clamped into [0, total_q)
+  int total_k;      // rows of K / V; likewise
+  int max_k;        // most keys per sequence
+};
+
+template <class T, int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_fwd_kernel(
     const char* __restrict__ q, const char* __restrict__ k, const char* __restrict__ v, char* __restrict__ o,
-    int batch, int hq, int hkv, int n, float c, int num_q_tiles) {
+    int batch, int hq, int hkv, int n, float c, int num_q_tiles, VarlenArgs vl) {
   using Cfg = PrefillCfg<D>;
   constexpr int NB = Cfg::NB;
   constexpr int KK = D / 16;  // 32x32x16 k-steps over the head dimension
@@ -157,30 +177,67 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // Non-causal: an XCD walks its heads one at a time, all query tiles of a
   // head back to back.  Causal: an XCD interleaves its heads and walks query
   // tiles longest-first, which balances the triangular work.
-  const int H = batch * hq;
-  int bh, qt;
-  if (H % 8 == 0) {
-    const int per = H / 8;
+  // Variable-length batches: (sequence, KV head) units are dealt round-robin
+  // to the XCDs instead, so that with hkv a multiple of 8 every XCD holds the
+  // same KV heads of every sequence -- unequal sequences then load all XCDs
+  // alike -- and the query heads sharing a KV head stay on one XCD; each XCD
+  // walks its units' query tiles from the last tile down.
+  int b, h, qt;
+  if constexpr (VARLEN) {
+    const int g = hq / hkv;
     const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
-    if (CAUSAL) {
-      bh = xcd * per + slot % per;
-      qt = num_q_tiles - 1 - slot / per;
-    } else {
-      bh = xcd * per + slot / num_q_tiles;
-      qt = slot % num_q_tiles;
-    }
+    const int per = (batch * hkv - xcd + 7) / 8 * g;  // work items of this XCD per query-tile index
+    if (slot >= per * num_q_tiles) return;            // (the whole workgroup)
+    qt = num_q_tiles - 1 - slot / per;
+    const int unit = xcd + 8 * ((slot % per) / g);
+    b = unit / hkv;
+    h = (unit % hkv) * g + (slot % per) % g;
   } else {
-    bh = blockIdx.x % H;
-    qt = CAUSAL ? num_q_tiles - 1 - (int)(blockIdx.x / H) : (int)(blockIdx.x / H);
+    const int H = batch * hq;
+    int bh;
+    if (H % 8 == 0) {
+      const int per = H / 8;
+      const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+      if (CAUSAL) {
+        bh = xcd * per + slot % per;
+        qt = num_q_tiles - 1 - slot / per;
+      } else {
+        bh = xcd * per + slot / num_q_tiles;
+        qt = slot % num_q_tiles;
+      }
+    } else {
+      bh = blockIdx.x % H;
+      qt = CAUSAL ? num_q_tiles - 1 - (int)(blockIdx.x / H) : (int)(blockIdx.x / H);
+    }
+    h = bh % hq;
+    b = bh / hq;
   }
-  const int h = bh % hq;
-  const int b = bh / hq;
   const int kvh = h / (hq / hkv);
 
   const int q0 = qt * Cfg::BR;
   const int qw = q0 + wave * 32 * NB;  // first query row of this wave; block blk covers qw + 32·blk ..
-  const size_t qo_base = ((size_t)b * hq + h) * (size_t)n * ROWB;
-  const size_t kv_base = ((size_t)b * hkv + kvh) * (size_t)n * ROWB;
+  // Rows of this (sequence, head): nq queries, nk keys, byte offsets of row 0
+  // and row strides.  The causal diagonal is shifted by off = nk - nq.
+  int nq = n, nk = n;
+  size_t qo_base, kv_base;
+  const uint32_t q_stride = VARLEN ? (uint32_t)hq * ROWB : ROWB;
+  const uint32_t kv_stride = VARLEN ? (uint32_t)hkv * ROWB : ROWB;
+  if constexpr (VARLEN) {
+    int qs = vl.cu_q[b], qe = vl.cu_q[b + 1], ks = vl.cu_k[b], ke = vl.cu_k[b + 1];
+    qs = min(max(qs, 0), vl.total_q);
+    qe = min(max(qe, qs), min(vl.total_q, qs + n));
+    ks = min(max(ks, 0), vl.total_k);
+    ke = min(max(ke, ks), min(vl.total_k, ks + vl.max_k));
+    nq = __builtin_amdgcn_readfirstlane(qe - qs);
+    nk = __builtin_amdgcn_readfirstlane(ke - ks);
+    if (q0 >= nq) return;  // past this sequence's last query tile (the whole workgroup)
+    qo_base = ((size_t)qs * hq + h) * ROWB;
+    kv_base = ((size_t)ks * hkv + kvh) * ROWB;
+  } else {
+    qo_base = ((size_t)b * hq + h) * (size_t)n * ROWB;
+    kv_base = ((size_t)b * hkv + kvh) * (size_t)n * ROWB;
+  }
+  const int off = VARLEN ? nk - nq : 0;
   const char* kp = k + kv_base;
   const char* vp = v + kv_base;
 
@@ -190,13 +247,36 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
   for (int blk = 0; blk < NB; ++blk) {
     const int qrow = qw + 32 * blk + l32;
-    const char* qp = q + qo_base + (size_t)qrow * ROWB;
+    const char* qp = q + qo_base + (size_t)qrow * q_stride;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) qf[blk][kk] = qrow < n ? gload16(qp + (kk * 16 + 8 * half) * 2) : zero4();
+    for (int kk = 0; kk < KK; ++kk) qf[blk][kk] = qrow < nq ? gload16(qp + (kk * 16 + 8 * half) * 2) : zero4();
   }
 
-  const int kend = CAUSAL ? min(n, q0 + Cfg::BR) : n;  // keys any row of this workgroup can see
+  // keys any row of this workgroup can see
+  const int kend = CAUSAL ? max(0, min(nk, q0 + Cfg::BR + off)) : nk;
   const int nkt = (kend + Cfg::BC - 1) / Cfg::BC;
+  auto store_rows = [&](auto value_of) ATTN_INLINE {  // O rows of this wave, element (blk, dt, e) -> float
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+      const int qrow = qw + 32 * blk + l32;
+      if (qrow < nq) {
+        char* op = o + qo_base + (size_t)qrow * q_stride;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int eh = 0; eh < 4; ++eh) {
+            const int dcol = dt * 32 + 8 * eh + 4 * half;
+            const u32x2 w = {T::pack2(value_of(blk, dt, 4 * eh + 0), value_of(blk, dt, 4 * eh + 1)),
+                             T::pack2(value_of(blk, dt, 4 * eh + 2), value_of(blk, dt, 4 * eh + 3))};
+            gstore8(op + dcol * 2, w);
+          }
+      }
+    }
+  };
+  if (VARLEN && nkt == 0) {  // no row of this workgroup sees a key: its rows are 0
+    store_rows([](int, int, int) ATTN_INLINE { return 0.f; });
+    return;
+  }
 
   // ---- tile fetch: 1 KB wave transfers straight into LDS.  Transfer g = i·WAVES + wave
   // fills bytes [g·1024, g·1024 + 1024) of the tile; lane l fills slot g·64 + l, i.e.
@@ -204,28 +284,31 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // Transfer groups start on multiples of 32 rows, so a lane's swizzle is the same in all.
   const int slot_row = (wave * 64 + lane) / Cfg::CPR;
   const int slot_chunk = lane % Cfg::CPR;
-  const uint32_t k_src = slot_row * ROWB + ((slot_chunk ^ swz_k<D>(slot_row)) * 16);
-  const uint32_t v_src = slot_row * ROWB + ((slot_chunk ^ swz_v<D>(slot_row)) * 16);
+  const uint32_t k_src = slot_row * kv_stride + ((slot_chunk ^ swz_k<D>(slot_row)) * 16);
+  const uint32_t v_src = slot_row * kv_stride + ((slot_chunk ^ swz_v<D>(slot_row)) * 16);
+  constexpr int GROUP_ROWS = Cfg::WAVES * 1024 / ROWB;  // rows of one transfer group
   constexpr int PT = 2 * Cfg::DMA;  // transfers per tile per wave: part j is tensor j&1 (K, V), group j>>1
   // Fetch cursor: scalar state of the next tile to fetch, advanced one tile at a
   // time so that issuing a transfer costs a handful of scalar instructions.
   int issued = 0;                                       // transfers this wave has issued so far
   const char* f_k = kp;                                 // K row j0 of the cursor's tile
   const char* f_v = vp;                                 // V row j0
-  uint32_t f_rem = (uint32_t)n * ROWB;                  // bytes from row j0 to the sequence end
+  uint32_t f_rem = (uint32_t)nk * kv_stride;            // bytes from row j0 to the sequence end
   const uint32_t f_dst0 = lds_addr(lds) + wave * 1024;  // this wave's transfers land at stage + g·1024
   uint32_t f_dst = f_dst0;                              // ... of the cursor's stage
   auto fetch_part = [&](int j) ATTN_INLINE {                        // transfer j of the cursor's tile
-    const uint32_t first = (j >> 1) * Cfg::WAVES * 1024;  // the transfer group's first byte in the tile
-    const uint32_t rec = f_rem > first ? f_rem - first : 0u;  // rows past the end read as 0
-    dma16_to_lds(bufres_words(((j & 1) ? f_v : f_k) + first, rec), (j & 1) ? v_src : k_src,
+    const uint32_t first = (j >> 1) * Cfg::WAVES * 1024;      // the transfer group's first byte in the tile
+    const uint32_t src = (j >> 1) * GROUP_ROWS * kv_stride;    // ... and in memory
+    const uint32_t rec = f_rem > src ? f_rem - src : 0u;      // rows past the end read as 0
+    dma16_to_lds(bufres_words(((j & 1) ? f_v : f_k) + src, rec), (j & 1) ? v_src : k_src,
                  f_dst + (j & 1) * Cfg::VREG + first);
     ++issued;
   };
   auto fetch_advance = [&]() ATTN_INLINE {
-    f_k += Cfg::BC * ROWB;
-    f_v += Cfg::BC * ROWB;
-    f_rem = f_rem > Cfg::BC * ROWB ? f_rem - Cfg::BC * ROWB : 0u;
+    const uint32_t step = Cfg::BC * kv_stride;
+    f_k += step;
+    f_v += step;
+    f_rem = f_rem > step ? f_rem - step : 0u;
     f_dst = f_dst + Cfg::TILE == f_dst0 + S * Cfg::TILE ? f_dst0 : f_dst + Cfg::TILE;
   };
   auto fetch_tile = [&]() ATTN_INLINE {
@@ -398,14 +481,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     return (ps[0] + ps[1]) + (ps[2] + ps[3]);
   };
   auto softmax = [&](int s0) ATTN_INLINE {
-    if (s0 + 32 > n || (CAUSAL && s0 + 31 > qw)) {
+    if (s0 + 32 > nk || (CAUSAL && s0 + 31 > qw + off)) {
 #pragma unroll
       for (int blk = 0; blk < NB; ++blk) {
-        const int qrow = qw + 32 * blk + l32;
+        const int qlim = qw + 32 * blk + l32 + off;  // last key this row sees under the causal mask
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key = s0 + 16 * (e >> 3) + 8 * half + (e & 7);
-          if (key >= n || (CAUSAL && key > qrow)) s[blk][e] = kNegInf;
+          if (key >= nk || (CAUSAL && key > qlim)) s[blk][e] = kNegInf;
         }
       }
     }
@@ -552,52 +635,57 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (grp == 0) step_end<true>();
 
   // ---- epilogue: O = o / l, rounded to the storage type, written once
+  float inv[NB];
 #pragma unroll
   for (int blk = 0; blk < NB; ++blk) {
     const float l_tot = sum_xor32(l_run[blk]);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const int qrow = qw + 32 * blk + l32;
-    if (qrow < n) {
-      char* op = o + qo_base + (size_t)qrow * ROWB;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int eh = 0; eh < 4; ++eh) {
-          const int dcol = dt * 32 + 8 * eh + 4 * half;
-          const u32x2 w = {T::pack2(oacc[blk][dt][4 * eh + 0] * inv, oacc[blk][dt][4 * eh + 1] * inv),
-                           T::pack2(oacc[blk][dt][4 * eh + 2] * inv, oacc[blk][dt][4 * eh + 3] * inv)};
-          gstore8(op + dcol * 2, w);
-        }
-    }
+    inv[blk] = l_tot > 0.f ? 1.f / l_tot : 0.f;
   }
+  store_rows([&](int blk, int dt, int e) ATTN_INLINE { return oacc[blk][dt][e] * inv[blk]; });
 }
 
-template <class T, int D, bool CAUSAL>
+template <class T, int D, bool CAUSAL, bool VARLEN>
 static hipError_t launch_prefill_t(const void* q, const void* k, const void* v, void* o, int batch, int hq, int hkv,
-                                   int n, float scale, hipStream_t stream) {
+                                   int n, float scale, VarlenArgs vl, hipStream_t stream) {
   using Cfg = PrefillCfg<D>;
   const int tiles = (n + Cfg::BR - 1) / Cfg::BR;
-  const long long blocks = (long long)tiles * hq * batch;
-  prefill_fwd_kernel<T, D, CAUSAL><<<dim3((unsigned)blocks), dim3(64 * Cfg::WAVES), 0, stream>>>(
+  // varlen: 8 XCDs x (units of the fullest XCD) x query heads per unit x tiles
+  const long long blocks = VARLEN ? 8LL * ((batch * hkv + 7) / 8) * (hq / hkv) * tiles : (long long)tiles * hq * batch;
+  prefill_fwd_kernel<T, D, CAUSAL, VARLEN><<<dim3((unsigned)blocks), dim3(64 * Cfg::WAVES), 0, stream>>>(
       static_cast<const char*>(q), static_cast<const char*>(k), static_cast<const char*>(v), static_cast<char*>(o),
-      batch, hq, hkv, n, scale * kLog2e, tiles);
+      batch, hq, hkv, n, scale * kLog2e, tiles, vl);
   return hipGetLastError();
 }
 
-template <class T, int D>
+template <class T, int D, bool VARLEN>
 static hipError_t launch_prefill_d(const void* q, const void* k, const void* v, void* o, int batch, int hq, int hkv,
-                                   int n, float scale, bool causal, hipStream_t stream) {
-  return causal ? launch_prefill_t<T, D, true>(q, k, v, o, batch, hq, hkv, n, scale, stream)
-                : launch_prefill_t<T, D, false>(q, k, v, o, batch, hq, hkv, n, scale, stream);
+                                   int n, float scale, bool causal, VarlenArgs vl, hipStream_t stream) {
+  return causal ? launch_prefill_t<T, D, true, VARLEN>(q, k, v, o, batch, hq, hkv, n, scale, vl, stream)
+                : launch_prefill_t<T, D, false, VARLEN>(q, k, v, o, batch, hq, hkv, n, scale, vl, stream);
+}
+
+template <bool VARLEN>
+static hipError_t launch_prefill_any(const void* q, const void* k, const void* v, void* o, bool bf16, int batch,
+                                     int hq, int hkv, int n, int d, float scale, bool causal, VarlenArgs vl,
+                                     hipStream_t stream) {
+  if (bf16)
+    return d == 64 ? launch_prefill_d<Bf16, 64, VARLEN>(q, k, v, o, batch, hq, hkv, n, scale, causal, vl, stream)
+                   : launch_prefill_d<Bf16, 128, VARLEN>(q, k, v, o, batch, hq, hkv, n, scale, causal, vl, stream);
+  return d == 64 ? launch_prefill_d<F16, 64, VARLEN>(q, k, v, o, batch, hq, hkv, n, scale, causal, vl, stream)
+                 : launch_prefill_d<F16, 128, VARLEN>(q, k, v, o, batch, hq, hkv, n, scale, causal, vl, stream);
 }
 
 hipError_t launch_prefill(const void* q, const void* k, const void* v, void* o, bool bf16, int batch, int hq,
                           int hkv, int n, int d, float scale, bool causal, hipStream_t stream) {
-  if (bf16)
-    return d == 64 ? launch_prefill_d<Bf16, 64>(q, k, v, o, batch, hq, hkv, n, scale, causal, stream)
-                   : launch_prefill_d<Bf16, 128>(q, k, v, o, batch, hq, hkv, n, scale, causal, stream);
-  return d == 64 ? launch_prefill_d<F16, 64>(q, k, v, o, batch, hq, hkv, n, scale, causal, stream)
-                 : launch_prefill_d<F16, 128>(q, k, v, o, batch, hq, hkv, n, scale, causal, stream);
+  return launch_prefill_any<false>(q, k, v, o, bf16, batch, hq, hkv, n, d, scale, causal,
+                                   VarlenArgs{nullptr, nullptr, 0, 0, 0}, stream);
+}
+
+hipError_t launch_prefill_varlen(const void* q, const void* k, const void* v, void* o, const int* cu_q,
+                                 const int* cu_k, int total_q, int total_k, int max_q, int max_k, bool bf16, int batch,
+                                 int hq, int hkv, int d, float scale, bool causal, hipStream_t stream) {
+  return launch_prefill_any<true>(q, k, v, o, bf16, batch, hq, hkv, max_q, d, scale, causal,
+                                  VarlenArgs{cu_q, cu_k, total_q, total_k, max_k}, stream);
 }
 
 }  // namespace attn

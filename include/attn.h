@@ -82,6 +82,40 @@ attn_status attn_prefill_fwd(const void* q, const void* k, const void* v, void* 
                              int hq, int hkv, int n, int d, float scale, int causal, void* stream);
 
 /*
+ * attn_prefill_varlen_fwd -- prefill / append over a packed batch of
+ * sequences of different lengths (the append / mixed kernel "with cu_seqlens"
+ * of "The four attention kernels you actually use", section 5 of "Attention
+ * Computation in Practice": chunked prefill, verifying a few speculative
+ * tokens).
+ *
+ * Sequence b owns query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and key
+ * rows cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1; call their counts nq and nk.
+ * Its queries are the LAST nq of its nk positions (bottom-right alignment),
+ * so with `causal` non-zero query i (0-based within the sequence) sees keys
+ * j <= i + nk - nq; without it every one of the nk keys.  nq = nk is the
+ * square problem of attn_prefill_fwd.  A query row that sees no key (nk = 0,
+ * or i + nk - nq < 0) is written as 0.
+ *
+ *   q, o : [total_q, hq,  d]  elements of `dtype`, token-major (packed)
+ *   k, v : [total_k, hkv, d]  elements of `dtype`, read only
+ *   cu_seqlens_q, cu_seqlens_k : [batch + 1] int32, DEVICE memory,
+ *          non-decreasing.  Preconditions: cu[0] >= 0, cu[batch] <= total,
+ *          each nq <= max_seqlen_q and nk <= max_seqlen_k.  The kernel clamps
+ *          every sequence into those bounds, so no access leaves the tensors.
+ *   total_q >= 1, total_k >= 0 : rows of the packed tensors
+ *   max_seqlen_q >= 1, max_seqlen_k >= 0 : bounds on nq and nk (the grid is
+ *          sized from max_seqlen_q)
+ *   scale, causal : as for attn_prefill_fwd
+ *
+ * Limits: total·heads·d below 2^40 for each tensor; max_seqlen_k·hkv·d·2 below
+ * 2^31 bytes (else ATTN_ERR_TOO_LARGE).  O must not alias Q, K or V.
+ */
+attn_status attn_prefill_varlen_fwd(const void* q, const void* k, const void* v, void* o, const int* cu_seqlens_q,
+                                    const int* cu_seqlens_k, int total_q, int total_k, int max_seqlen_q,
+                                    int max_seqlen_k, int dtype, int batch, int hq, int hkv, int d, float scale,
+                                    int causal, void* stream);
+
+/*
  * Split-K ("Flash-Decoding") single-query decode, in two calls: partial states
  * per key slice, then their merge.  Splitting the cache sequence across
  * workgroups is what lets one query fill the GPU ("Prefill and decode are

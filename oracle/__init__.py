@@ -14,6 +14,7 @@ invariants, special cases and a library routine; none is "parity unpinned".
 from .attention import (  # noqa: F401
     attention,
     attention_rows,
+    attention_varlen,
     decode,
     decode_paged,
     gather_pages,

@@ -36,7 +36,9 @@ Readings where the pages are silent (each is listed in the design doc):
 
 * A row with no visible key (decode with ``kv_len = 0``, an all-empty merge)
   returns 0.  The pages leave softmax over no keys undefined.
-* Causal attention is only defined for square problems here.
+* ``attention`` takes square causal problems only; ``attention_varlen``
+  places a sequence's ``nq`` queries at its last ``nq`` positions
+  (bottom-right alignment), which is the square rule when ``nq = nk``.
 
 ``online_softmax_tiled`` and ``split_partials`` are second implementations used
 only by the oracle's own self-tests: the recurrence of "The online softmax" and
@@ -109,6 +111,35 @@ def attention(q, k, v, scale: float, causal: bool = False, row_block: int = 256)
                 i1 = min(N, i0 + row_block)
                 rows = np.arange(i0, i1) if causal else None
                 out[b, h, i0:i1] = _materialised_rows(q[b, h, i0:i1], k[b, kh], v[b, kh], scale, rows)
+    return out
+
+
+def attention_varlen(q, k, v, cu_q, cu_k, scale: float, causal: bool = False):
+    """Exact attention over a packed batch of sequences of different lengths.
+
+    ``q: [total_q, Hq, d]`` and ``k, v: [total_k, Hkv, d]`` (token-major);
+    sequence ``b`` owns query rows ``cu_q[b] .. cu_q[b+1]-1`` and key rows
+    ``cu_k[b] .. cu_k[b+1]-1`` (the varlen "cu_seqlens" kernels of "The four
+    attention kernels you actually use", section 5 of "Attention Computation
+    in Practice").  Its ``nq`` queries are the last ``nq`` of its ``nk``
+    positions, so query ``i`` stands at position ``i + nk - nq`` and, under
+    the causal rule ``j <= position`` ("Masking variants", same section),
+    sees keys ``0 .. i + nk - nq``.  A query that sees no key gives 0.
+    Returns ``O: [total_q, Hq, d]`` in fp64 (rows owned by no sequence are 0).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    total_q, Hq, d = q.shape
+    Hkv = k.shape[1]
+    out = np.zeros((total_q, Hq, d))
+    for b in range(len(cu_q) - 1):
+        qs, qe, ks, ke = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        nq, nk = qe - qs, ke - ks
+        if nq < 0 or nk < 0:
+            raise ValueError(f"sequence {b}: offsets decrease")
+        positions = np.arange(nq) + (nk - nq) if causal else None
+        for h in range(Hq):
+            kh = kv_head_of(h, Hq, Hkv)
+            out[qs:qe, h] = _materialised_rows(q[qs:qe, h], k[ks:ke, kh], v[ks:ke, kh], scale, positions)
     return out
 
 

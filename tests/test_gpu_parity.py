@@ -113,6 +113,115 @@ def test_prefill_full_size_sampled_rows(A, name):
             assert_close(out[b, h, rows], ref, f"{w.name} b={b} h={h}")
 
 
+# --- varlen / append prefill ------------------------------------------------------------
+
+def varlen_case(A, w, nq, nk, seed=0):
+    announce(f"varlen {w.name} nq={nq[:8]} nk={nk[:8]}")
+    q, k, v, cu_q, cu_k = w_inputs = workloads.varlen_inputs(w, device=DEV, salt=seed, nq=nq, nk=nk)
+    out = A.prefill_varlen_fwd(q, k, v, cu_q.to(DEV), cu_k.to(DEV), max(nq), max(nk), causal=w.causal,
+                               scale=w.scale)
+    torch.cuda.synchronize()
+    ref = oracle.attention_varlen(f64(q), f64(k), f64(v), cu_q.numpy(), cu_k.numpy(), w.scale, w.causal)
+    assert_close(out, ref, f"varlen {w.name}")
+    return w_inputs, out
+
+
+def varlen_w(hq, hkv, d, causal, dtype):
+    return workloads.Varlen(f"varlen_case_{hq}_{hkv}_{d}_{int(causal)}_{dtype}", 1, hq, hkv, d, causal, dtype,
+                            (1, 1), (0, 0))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_mixed_lengths(A, causal, d, dtype):
+    """Appends of 1..700 queries onto 0..1200 cached positions, an empty query
+    list, a sequence with no keys, more queries than keys, tile-edge lengths."""
+    nq = [1, 0, 5, 300, 17, 64, 700, 256, 40]
+    nk = [1, 9, 0, 300, 1200, 65, 900, 511, 20]
+    varlen_case(A, varlen_w(8, 2, d, causal, dtype), nq, nk)
+
+
+@pytest.mark.parametrize("hq,hkv", [(1, 1), (8, 8), (16, 2), (12, 1)])
+def test_varlen_heads_and_gqa(A, hq, hkv):
+    varlen_case(A, varlen_w(hq, hkv, 128, True, "bf16"), [130, 3, 513], [1000, 4, 513])
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_equal_lengths_match_square_kernel_bitwise(A, d, causal):
+    """A batch of equal square sequences through the varlen kernel gives the
+    square kernel's output bit for bit (same tiles, same arithmetic)."""
+    B, hq, hkv, n = 3, 4, 2, 700
+    w = workloads.Prefill(f"varlen_sq_{d}_{int(causal)}", B, hq, hkv, n, d, causal, "bf16")
+    announce(w.name)
+    q, k, v = (t.to(DEV) for t in workloads.prefill_inputs(w))
+    sq = A.prefill_fwd(q, k, v, causal=causal, scale=w.scale)
+    cu = torch.arange(0, (B + 1) * n, n, dtype=torch.int32, device=DEV)
+    pq = q.transpose(1, 2).reshape(B * n, hq, d).contiguous()
+    pk = k.transpose(1, 2).reshape(B * n, hkv, d).contiguous()
+    pv = v.transpose(1, 2).reshape(B * n, hkv, d).contiguous()
+    out = A.prefill_varlen_fwd(pq, pk, pv, cu, cu, n, n, causal=causal, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, sq.transpose(1, 2).reshape(B * n, hq, d))
+
+
+def test_varlen_clamps_offsets_into_the_tensors(A):
+    """Offsets past the packed tensors are clamped to their ends, and a
+    sequence longer than max_seqlen_k to its first max_seqlen_k keys: the
+    kernel reads and writes only inside the tensors."""
+    w = varlen_w(4, 2, 64, True, "bf16")
+    announce("varlen clamp")
+    q, k, v, cu_q, cu_k = workloads.varlen_inputs(w, device=DEV, nq=[50, 60], nk=[80, 70])
+    bad_q = torch.tensor([0, 50, 999], dtype=torch.int32)  # the second sequence runs past total_q = 110
+    bad_k = torch.tensor([0, 80, 4000], dtype=torch.int32)  # ... and past total_k = 150
+    out = torch.zeros_like(q)
+    A.prefill_varlen_fwd(q, k, v, bad_q.to(DEV), bad_k.to(DEV), 60, 80, causal=True, scale=w.scale, out=out)
+    torch.cuda.synchronize()
+    ref = oracle.attention_varlen(f64(q), f64(k), f64(v), [0, 50, 110], [0, 80, 150], w.scale, True)
+    assert_close(out, ref, "varlen clamp")
+    # max_seqlen_k = 70 keeps the first sequence's first 70 keys (its queries then stand at 20 .. 69)
+    out = torch.zeros_like(q)
+    A.prefill_varlen_fwd(q, k, v, cu_q.to(DEV), cu_k.to(DEV), 60, 70, causal=True, scale=w.scale, out=out)
+    torch.cuda.synchronize()
+    ref0 = oracle.attention_varlen(f64(q[:50]), f64(k[:70]), f64(v[:70]), [0, 50], [0, 70], w.scale, True)
+    assert_close(out[:50], ref0, "varlen clamp to max_seqlen_k")
+
+
+def test_varlen_speculative_verify_shapes(A):
+    """A few queries (1..8 draft tokens) against long caches."""
+    varlen_case(A, varlen_w(32, 8, 128, True, "bf16"), [1, 4, 8, 2], [5000, 3000, 4097, 64])
+
+
+VAR = workloads.WORKLOADS["append_causal_b16_hq32_hkv8_d128_q256to2048_past0to16384_bf16"]
+
+
+def test_varlen_append_full_sampled(A):
+    """The benchmarked append batch (16 sequences, 256..2048 new queries on
+    0..16384 cached positions, 32/8 heads, d=128, causal) at full size; sampled
+    rows of every sequence (its first and last 64 queries and 64 random ones, 4
+    query heads each) against the oracle computed row by row."""
+    announce(VAR.name)
+    q, k, v, cu_q, cu_k = workloads.varlen_inputs(VAR, device=DEV)
+    nq, nk = VAR.lengths()
+    out = A.prefill_varlen_fwd(q, k, v, cu_q.to(DEV), cu_k.to(DEV), max(nq), max(nk), causal=True,
+                               scale=VAR.scale)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any()
+    rng = np.random.default_rng(9)
+    g = VAR.hq // VAR.hkv
+    for b in range(VAR.batch):
+        rows = sorted({*range(min(64, nq[b])), *range(max(0, nq[b] - 64), nq[b]),
+                       *rng.integers(0, nq[b], 64).tolist()})
+        rows = np.array(rows)
+        qs, ks = int(cu_q[b]), int(cu_k[b])
+        for h in rng.choice(VAR.hq, 4, replace=False):
+            K = f64(k[ks:ks + nk[b], h // g])
+            V = f64(v[ks:ks + nk[b], h // g])
+            ref = oracle.attention_rows(f64(q[qs + rows, h]), K, V, VAR.scale, rows + nk[b] - nq[b])
+            assert_close(out[qs + rows, h], ref, f"{VAR.name} b={b} h={h}")
+
+
 # --- decode ----------------------------------------------------------------------------
 
 def decode_case(A, w, kv_lens, max_len, batch, num_splits, check_partials=True, seed=0):

@@ -307,6 +307,105 @@ def test_decode_with_no_keys_is_zero():
     assert np.array_equal(out, np.zeros((1, 2, 8)))
 
 
+# --- varlen / append ("The four attention kernels you actually use", "Masking variants",
+# "Attention Computation in Practice" section 5) ---
+
+def pack(seqs):
+    """[H, n, d] arrays -> token-major [Σn, H, d] and offsets."""
+    cu = np.cumsum([0] + [x.shape[1] for x in seqs])
+    return np.concatenate([x.transpose(1, 0, 2) for x in seqs], axis=0), cu
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_square_sequences_equal_square_attention(causal):
+    hq, hkv, d = 4, 2, 16
+    ns = [1, 7, 40, 33]
+    qs = [gauss(80 + i, hq, n, d) for i, n in enumerate(ns)]
+    ks = [gauss(90 + i, hkv, n, d) for i, n in enumerate(ns)]
+    vs = [gauss(100 + i, hkv, n, d) for i, n in enumerate(ns)]
+    (q, cu), (k, _), (v, _) = pack(qs), pack(ks), pack(vs)
+    out = oracle.attention_varlen(q, k, v, cu, cu, 0.3, causal)
+    for i, n in enumerate(ns):
+        ref = oracle.attention(qs[i][None], ks[i][None], vs[i][None], 0.3, causal)[0]
+        assert np.max(np.abs(out[cu[i]:cu[i + 1]].transpose(1, 0, 2) - ref)) <= TOL
+
+
+def test_varlen_append_chunks_reassemble_causal_prefill():
+    """Causal prefill of 50 positions = three appended chunks [0, 12), [12, 31),
+    [31, 50), each attending to every key up to its own end: the queries sit at
+    the END of each chunk's keys (bottom-right), not at the start."""
+    d, n = 8, 50
+    q, k, v = gauss(110, 1, n, d), gauss(111, 1, n, d), gauss(112, 1, n, d)
+    full = oracle.attention(q[None], k[None], v[None], 0.35, True)[0, 0]
+    for c0, c1 in ((0, 12), (12, 31), (31, 50)):
+        qc = q[0, c0:c1][:, None]
+        kc, vc = k[0, :c1][:, None], v[0, :c1][:, None]
+        out = oracle.attention_varlen(qc, kc, vc, [0, c1 - c0], [0, c1], 0.35, True)[:, 0]
+        assert np.max(np.abs(out - full[c0:c1])) <= TOL
+        if c0 > 0:  # top-left alignment would differ
+            top_left = oracle.attention(np.pad(qc[:, 0], ((0, c0), (0, 0)))[None, None][:, :, :c1],
+                                        kc[:, 0][None, None], vc[:, 0][None, None], 0.35, True)[0, 0, :c1 - c0]
+            assert np.max(np.abs(top_left - full[c0:c1])) > 1e-3
+
+
+def test_varlen_single_query_is_decode():
+    hq, hkv, d = 6, 3, 8
+    nks = [5, 1, 30]
+    q = gauss(113, len(nks), hq, d)
+    kc, vc = gauss(114, len(nks), hkv, 30, d), gauss(115, len(nks), hkv, 30, d)
+    kp = np.concatenate([kc[b, :, :n].transpose(1, 0, 2) for b, n in enumerate(nks)])
+    vp = np.concatenate([vc[b, :, :n].transpose(1, 0, 2) for b, n in enumerate(nks)])
+    cu_k = np.cumsum([0] + nks)
+    for causal in (False, True):
+        out = oracle.attention_varlen(q, kp, vp, np.arange(len(nks) + 1), cu_k, 0.4, causal)
+        assert np.max(np.abs(out - oracle.decode(q, kc, vc, nks, 0.4))) <= TOL
+
+
+def test_varlen_more_queries_than_keys():
+    """nq = 5 over nk = 3 keys, causal: the first two queries stand before
+    every key and give 0; query 2 sees only key 0 and returns its V row exactly."""
+    d = 4
+    q, k, v = gauss(116, 5, 1, d), gauss(117, 3, 1, d), gauss(118, 3, 1, d)
+    out = oracle.attention_varlen(q, k, v, [0, 5], [0, 3], 0.5, True)[:, 0]
+    assert np.array_equal(out[:2], np.zeros((2, d)))
+    assert np.array_equal(out[2], v[0, 0])
+    full = oracle.attention(q[2:, 0][None, None], k[:, 0][None, None], v[:, 0][None, None], 0.5, True)[0, 0]
+    assert np.max(np.abs(out[2:] - full)) <= TOL
+
+
+def test_varlen_matches_sdpa_with_bottom_right_mask():
+    """Library attention with an explicit boolean mask j <= i + nk - nq, built
+    here from the definition, on a packed GQA batch with an empty sequence."""
+    hq, hkv, d = 4, 2, 8
+    nq, nk = [3, 0, 9, 16], [10, 4, 9, 20]
+    cu_q, cu_k = np.cumsum([0] + nq), np.cumsum([0] + nk)
+    q, k, v = gauss(119, cu_q[-1], hq, d), gauss(120, cu_k[-1], hkv, d), gauss(121, cu_k[-1], hkv, d)
+    out = oracle.attention_varlen(q, k, v, cu_q, cu_k, 0.3, True)
+    for b in range(len(nq)):
+        if nq[b] == 0:
+            continue
+        mask = np.arange(nk[b])[None, :] <= np.arange(nq[b])[:, None] + nk[b] - nq[b]
+        tq = torch.from_numpy(q[cu_q[b]:cu_q[b + 1]].transpose(1, 0, 2).copy())
+        tk = torch.from_numpy(k[cu_k[b]:cu_k[b + 1]].transpose(1, 0, 2).copy()).repeat_interleave(2, dim=0)
+        tv = torch.from_numpy(v[cu_k[b]:cu_k[b + 1]].transpose(1, 0, 2).copy()).repeat_interleave(2, dim=0)
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.from_numpy(mask),
+                                                               scale=0.3)
+        assert np.max(np.abs(out[cu_q[b]:cu_q[b + 1]] - ref.numpy().transpose(1, 0, 2))) <= TOL
+
+
+def test_varlen_visible_pair_count():
+    w = workloads.Varlen("t", 3, 1, 1, 64, True, "bf16", (1, 1), (0, 0))
+    # nq=nk=4: 1+2+3+4; nq=2 of nk=5: 4+5; nq=5 of nk=3: 0+0+1+2+3
+    assert w.visible_pairs([4, 2, 5], [4, 5, 3]) == 10 + 9 + 6
+    w2 = dataclasses_replace(w, causal=False)
+    assert w2.visible_pairs([4, 2, 5], [4, 5, 3]) == 16 + 10 + 15
+
+
+def dataclasses_replace(w, **kw):
+    import dataclasses
+    return dataclasses.replace(w, **kw)
+
+
 # --- paged decode ("PagedAttention's kernel difference", "Attention Computation in Practice" section 5) ---
 
 def test_gather_pages_reads_the_listed_blocks_in_order():

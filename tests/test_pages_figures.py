@@ -61,7 +61,7 @@ def test_prefill_flops_count_visible_pairs(n, causal):
 
 def test_workload_shapes():
     W = workloads.WORKLOADS
-    assert len(W) == 6
+    assert len(W) == 7
     c3 = W["prefill_causal_gqa_b1_hq32_hkv8_n32768_d128_bf16"]
     assert math.isclose(c3.flops(), 8.796e12, rel_tol=1e-3)
     c2 = W["prefill_b4_h32_n4096_d128_bf16"]
@@ -71,6 +71,13 @@ def test_workload_shapes():
     for w in W.values():
         assert w.hq % w.hkv == 0
         assert w.scale == pytest.approx(1 / math.sqrt(w.d), rel=1e-7)
+
+
+def test_append_lengths_are_seeded_and_in_range():
+    w = workloads.WORKLOADS["append_causal_b16_hq32_hkv8_d128_q256to2048_past0to16384_bf16"]
+    (nq, nk), (nq2, nk2) = w.lengths(), w.lengths()
+    assert nq == nq2 and nk == nk2 and len(nq) == w.batch
+    assert all(256 <= a <= 2048 and 0 <= b - a <= 16384 for a, b in zip(nq, nk))
 
 
 def test_ragged_lengths_are_seeded_and_in_range():

@@ -27,7 +27,7 @@ import torch
 
 BASE_SEED = 20240601
 
-TENSOR_IDS = {"q": 1, "k": 2, "v": 3, "kv_lens": 4}
+TENSOR_IDS = {"q": 1, "k": 2, "v": 3, "kv_lens": 4, "lens": 5, "pages": 6}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -84,6 +84,52 @@ class Decode:
         return 2.0 * self.hkv * self.d * 2 * total_len
 
 
+@dataclasses.dataclass(frozen=True)
+class Varlen:
+    """A packed batch of sequences of different lengths (append / chunked
+    prefill): sequence b appends ``nq_b`` new queries to ``past_b`` cached
+    positions, so it has ``nk_b = past_b + nq_b`` keys and its queries are the
+    last ``nq_b`` positions.  Q, O ``[Σnq, Hq, d]``; K, V ``[Σnk, Hkv, d]``."""
+
+    name: str
+    batch: int
+    hq: int
+    hkv: int
+    d: int
+    causal: bool
+    dtype: str
+    q_range: tuple     # inclusive range of nq
+    past_range: tuple  # inclusive range of past
+
+    @property
+    def scale(self) -> float:
+        return fp32_scale(self.d)
+
+    def lengths(self, salt: int = 0):
+        """Seeded (nq, nk) per sequence: integers uniform on the inclusive ranges."""
+        gen = torch.Generator()
+        gen.manual_seed(seed_for(self.name, "lens", salt) & ((1 << 63) - 1))
+        nq = torch.randint(self.q_range[0], self.q_range[1] + 1, (self.batch,), generator=gen)
+        past = torch.randint(self.past_range[0], self.past_range[1] + 1, (self.batch,), generator=gen)
+        return [int(x) for x in nq], [int(a + b) for a, b in zip(past, nq)]
+
+    def visible_pairs(self, nq, nk) -> int:
+        """(query, key) pairs the mask leaves visible: all ``nq·nk`` without it;
+        with it query i sees ``clamp(i + nk - nq + 1, 0, nk)`` keys."""
+        total = 0
+        for a, b in zip(nq, nk):
+            if not self.causal:
+                total += a * b
+                continue
+            i = torch.arange(a, dtype=torch.int64)
+            total += int(torch.clamp(i + (b - a) + 1, 0, b).sum())
+        return total
+
+    def flops(self, nq, nk) -> float:
+        """Algorithmic FLOPs: 4·d per visible (query, key) pair per query head."""
+        return 4.0 * self.d * self.hq * self.visible_pairs(nq, nk)
+
+
 def fp32_scale(d: int) -> float:
     """1/sqrt(d) rounded to fp32 -- the exact value the kernels receive."""
     return float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32).item())
@@ -97,6 +143,8 @@ WORKLOADS = {
         Prefill("prefill_b4_h32_n4096_d128_bf16", 4, 32, 32, 4096, 128, False, "bf16"),
         Prefill("prefill_causal_gqa_b1_hq32_hkv8_n32768_d128_bf16", 1, 32, 8, 32768, 128, True, "bf16"),
         Decode("decode_b1_hq32_hkv8_d128_len262144_bf16", 1, 32, 8, 128, 262144, None, 1.0, "bf16"),
+        Varlen("append_causal_b16_hq32_hkv8_d128_q256to2048_past0to16384_bf16", 16, 32, 8, 128, True, "bf16",
+               (256, 2048), (0, 16384)),
         Decode("decode_ragged_b64_hq64_hkv8_d128_len1024to32768_q8_bf16", 64, 64, 8, 128, 32768,
                (1024, 32768), 8.0, "bf16"),
     ]
@@ -128,6 +176,19 @@ def prefill_inputs(w: Prefill, device="cpu", salt: int = 0, n: Optional[int] = N
     k = normal((w.batch, w.hkv, n, w.d), w.dtype, seed_for(w.name, "k", salt), device)
     v = normal((w.batch, w.hkv, n, w.d), w.dtype, seed_for(w.name, "v", salt), device)
     return q, k, v
+
+
+def varlen_inputs(w: Varlen, device="cpu", salt: int = 0, nq=None, nk=None):
+    """Packed q ``[Σnq, Hq, d]``, k and v ``[Σnk, Hkv, d]`` and the int32
+    offsets ``cu_q``, ``cu_k`` (CPU) for the given or the seeded lengths."""
+    if nq is None or nk is None:
+        nq, nk = w.lengths(salt)
+    cu_q = torch.tensor([0] + list(nq), dtype=torch.int64).cumsum(0).to(torch.int32)
+    cu_k = torch.tensor([0] + list(nk), dtype=torch.int64).cumsum(0).to(torch.int32)
+    q = normal((int(cu_q[-1]), w.hq, w.d), w.dtype, seed_for(w.name, "q", salt), device)
+    k = normal((int(cu_k[-1]), w.hkv, w.d), w.dtype, seed_for(w.name, "k", salt), device)
+    v = normal((int(cu_k[-1]), w.hkv, w.d), w.dtype, seed_for(w.name, "v", salt), device)
+    return q, k, v, cu_q, cu_k
 
 
 def decode_lengths(w: Decode, salt: int = 0) -> torch.Tensor:
