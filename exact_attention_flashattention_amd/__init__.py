@@ -79,10 +79,13 @@ def prefill_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool 
 
 def prefill_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
                        cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int, causal: bool = False,
-                       scale: Optional[float] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                       scale: Optional[float] = None, out: Optional[torch.Tensor] = None, window: int = 0,
+                       alibi_slopes: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Packed variable-length prefill / append: ``q [total_q, Hq, d]``, ``k, v [total_k, Hkv, d]``,
     ``cu_seqlens_*`` int32 device tensors of ``batch + 1`` offsets; returns ``[total_q, Hq, d]``.
-    Queries are bottom-right aligned: query i of a sequence sees keys j <= i + nk - nq when causal."""
+    Queries are bottom-right aligned: query i of a sequence (position p = i + nk - nq) sees keys j <= p when
+    causal, and only p - window < j when ``window > 0``; ``alibi_slopes`` (fp32 device ``[Hq]``) adds
+    ``-slope·(p - j)`` to each score."""
     lib = _lib_handle()
     if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape:
         raise ValueError("expected q [total_q, Hq, d] and k, v [total_k, Hkv, d]")
@@ -95,12 +98,16 @@ def prefill_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seq
             raise ValueError(f"{name} must be a 1-D int32 device tensor")
     if cu_seqlens_k.numel() != cu_seqlens_q.numel() or cu_seqlens_q.numel() < 2:
         raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold batch + 1 >= 2 offsets")
+    if alibi_slopes is not None and (alibi_slopes.dtype != torch.float32 or alibi_slopes.numel() != hq
+                                     or alibi_slopes.device != q.device):
+        raise ValueError("alibi_slopes must be a float32 device tensor with one slope per query head")
     if out is None:
         out = torch.empty_like(q)
     st = lib.attn_prefill_varlen_fwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
                                      _dev(cu_seqlens_q, "cu_seqlens_q"), _dev(cu_seqlens_k, "cu_seqlens_k"), total_q,
                                      total_k, int(max_seqlen_q), int(max_seqlen_k), _dtype_code(q),
                                      cu_seqlens_q.numel() - 1, hq, hkv, d, _scale(scale, d), int(bool(causal)),
+                                     int(window), None if alibi_slopes is None else _dev(alibi_slopes, "alibi_slopes"),
                                      _stream(q))
     _lib.check("attn_prefill_varlen_fwd", st)
     return out

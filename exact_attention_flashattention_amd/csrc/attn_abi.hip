@@ -70,12 +70,12 @@ attn_status attn_prefill_fwd(const void* q, const void* k, const void* v, void* 
 attn_status attn_prefill_varlen_fwd(const void* q, const void* k, const void* v, void* o, const int* cu_seqlens_q,
                                     const int* cu_seqlens_k, int total_q, int total_k, int max_seqlen_q,
                                     int max_seqlen_k, int dtype, int batch, int hq, int hkv, int d, float scale,
-                                    int causal, void* stream) {
+                                    int causal, int window, const float* alibi_slopes, void* stream) {
   if (!q || !k || !v || !o || !cu_seqlens_q || !cu_seqlens_k) return ATTN_ERR_NULL_PTR;
   if (batch < 1 || hq < 1 || hkv < 1 || total_q < 1 || total_k < 0 || max_seqlen_q < 1 || max_seqlen_k < 0 ||
-      hq % hkv != 0 || !scale_ok(scale))
+      hq % hkv != 0 || !scale_ok(scale) || window < 0)
     return ATTN_ERR_BAD_SHAPE;
-  if ((d != 64 && d != 128) || !dtype_ok(dtype)) return ATTN_ERR_UNSUPPORTED;
+  if ((d != 64 && d != 128) || !dtype_ok(dtype) || (window > 0 && !causal)) return ATTN_ERR_UNSUPPORTED;
   // per-sequence K/V byte ranges are 32-bit buffer offsets; the grid is one-dimensional
   const long long tiles = (max_seqlen_q + 255) / 256 + 1;  // at least the kernel's query tiles (>= 256 rows each)
   const long long blocks = 8LL * (((long long)batch * hkv + 7) / 8) * (hq / hkv) * tiles;
@@ -85,7 +85,7 @@ attn_status attn_prefill_varlen_fwd(const void* q, const void* k, const void* v,
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_MISALIGNED;
   return from_hip(attn::launch_prefill_varlen(q, k, v, o, cu_seqlens_q, cu_seqlens_k, total_q, total_k, max_seqlen_q,
                                               max_seqlen_k, dtype == ATTN_BF16, batch, hq, hkv, d, scale,
-                                              causal != 0, static_cast<hipStream_t>(stream)));
+                                              causal != 0, window, alibi_slopes, static_cast<hipStream_t>(stream)));
 }
 
 int attn_decode_num_splits(int batch, int hkv, int max_kv_len) {

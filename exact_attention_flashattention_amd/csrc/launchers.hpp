@@ -14,7 +14,8 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, void* o, 
 // sequence b owns rows cu_q[b] .. cu_q[b+1]-1 and cu_k[b] .. cu_k[b+1]-1.
 hipError_t launch_prefill_varlen(const void* q, const void* k, const void* v, void* o, const int* cu_q,
                                  const int* cu_k, int total_q, int total_k, int max_q, int max_k, bool bf16, int batch,
-                                 int hq, int hkv, int d, float scale, bool causal, hipStream_t stream);
+                                 int hq, int hkv, int d, float scale, bool causal, int window, const float* alibi,
+                                 hipStream_t stream);
 
 hipError_t launch_decode_splitk(const void* q, const void* k_cache, const void* v_cache, const int* kv_lens,
                                 int max_kv_len, bool bf16, int batch, int hq, int hkv, int d, float scale,

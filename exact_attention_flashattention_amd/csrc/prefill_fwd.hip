@@ -56,6 +56,14 @@
 // are the row strides (a runtime value instead of the row size), the
 // per-sequence bases and lengths, and workgroups past a sequence's last query
 // tile returning at once.
+//
+// Masking variants of the same section, both run-time options: a sliding
+// window W keeps key j for the query at position p iff p - W < j <= p (the
+// workgroup starts at the first key tile its first row's window reaches, so
+// the window skips tiles on the left as the diagonal skips them on the
+// right); ALiBi adds -m_h·(p - j) to every score of query head h (slopes m_h
+// given per query head), folded into the raw scores as (m_h / scale)·(j - p)
+// before the exponentials.
 #include "device_common.hpp"
 #include "launchers.hpp"
 
@@ -150,10 +158,16 @@ struct VarlenArgs {
   int max_k;        // most keys per sequence
 };
 
+// Masking variants (zero / null: none).
+struct MaskArgs {
+  int window;          // > 0: sliding window of this many keys (causal kernels only)
+  const float* alibi;  // [hq] ALiBi slopes, natural-log units per position
+};
+
 template <class T, int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_fwd_kernel(
     const char* __restrict__ q, const char* __restrict__ k, const char* __restrict__ v, char* __restrict__ o,
-    int batch, int hq, int hkv, int n, float c, int num_q_tiles, VarlenArgs vl) {
+    int batch, int hq, int hkv, int n, float c, int num_q_tiles, VarlenArgs vl, MaskArgs mk) {
   using Cfg = PrefillCfg<D>;
   constexpr int NB = Cfg::NB;
   constexpr int KK = D / 16;  // 32x32x16 k-steps over the head dimension
@@ -252,9 +266,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int kk = 0; kk < KK; ++kk) qf[blk][kk] = qrow < nq ? gload16(qp + (kk * 16 + 8 * half) * 2) : zero4();
   }
 
-  // keys any row of this workgroup can see
+  // keys any row of this workgroup can see: [key0, kend), key0 a tile boundary
   const int kend = CAUSAL ? max(0, min(nk, q0 + Cfg::BR + off)) : nk;
-  const int nkt = (kend + Cfg::BC - 1) / Cfg::BC;
+  const int window = (CAUSAL && VARLEN) ? mk.window : 0;  // the options come with the varlen entry point
+  const int key0 = window > 0 ? max(0, q0 + off - window + 1) / Cfg::BC * Cfg::BC : 0;
+  const int nkt = VARLEN ? max(0, (kend + Cfg::BC - 1) / Cfg::BC - key0 / Cfg::BC)  // tiles to process
+                         : (kend + Cfg::BC - 1) / Cfg::BC;
+  // ALiBi slope of this head in raw-score units (the scores are scaled by c = scale·log2 e later)
+  const bool alibi = VARLEN && mk.alibi != nullptr;
+  const float alibi_raw = alibi ? mk.alibi[h] * kLog2e / c : 0.f;
   auto store_rows = [&](auto value_of) ATTN_INLINE {  // O rows of this wave, element (blk, dt, e) -> float
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
@@ -291,9 +311,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // Fetch cursor: scalar state of the next tile to fetch, advanced one tile at a
   // time so that issuing a transfer costs a handful of scalar instructions.
   int issued = 0;                                       // transfers this wave has issued so far
-  const char* f_k = kp;                                 // K row j0 of the cursor's tile
-  const char* f_v = vp;                                 // V row j0
-  uint32_t f_rem = (uint32_t)nk * kv_stride;            // bytes from row j0 to the sequence end
+  const char* f_k = kp + (size_t)key0 * kv_stride;      // K row j0 of the cursor's tile
+  const char* f_v = vp + (size_t)key0 * kv_stride;      // V row j0
+  uint32_t f_rem = (uint32_t)(nk - key0) * kv_stride;   // bytes from row j0 to the sequence end
   const uint32_t f_dst0 = lds_addr(lds) + wave * 1024;  // this wave's transfers land at stage + g·1024
   uint32_t f_dst = f_dst0;                              // ... of the cursor's stage
   auto fetch_part = [&](int j) ATTN_INLINE {                        // transfer j of the cursor's tile
@@ -481,15 +501,37 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     return (ps[0] + ps[1]) + (ps[2] + ps[3]);
   };
   auto softmax = [&](int s0) ATTN_INLINE {
-    if (s0 + 32 > nk || (CAUSAL && s0 + 31 > qw + off)) {
+    if (s0 + 32 > nk || (CAUSAL && s0 + 31 > qw + off) ||
+        (window > 0 && s0 <= qw + 32 * NB - 1 + off - window)) {
 #pragma unroll
       for (int blk = 0; blk < NB; ++blk) {
-        const int qlim = qw + 32 * blk + l32 + off;  // last key this row sees under the causal mask
+        const int qlim = qw + 32 * blk + l32 + off;  // this row's position: the last key it sees if causal
+        if constexpr (VARLEN) {
+          // visible keys of this row: [lo, hi]; one unsigned range test per score
+          // (key - lo wraps past span for keys below lo; an empty range masks all)
+          const int hi = CAUSAL ? min(qlim, nk - 1) : nk - 1;
+          const int lo = window > 0 ? max(qlim - window + 1, 0) : 0;
+          const uint32_t lo_u = hi >= lo ? (uint32_t)lo : 0x80000000u;
+          const uint32_t span = hi >= lo ? (uint32_t)(hi - lo) : 0u;
+          const uint32_t base = (uint32_t)(s0 + 8 * half) - lo_u;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = s0 + 16 * (e >> 3) + 8 * half + (e & 7);
-          if (key >= nk || (CAUSAL && key > qlim)) s[blk][e] = kNegInf;
+          for (int e = 0; e < 16; ++e)
+            if (base + (uint32_t)(16 * (e >> 3) + (e & 7)) > span) s[blk][e] = kNegInf;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = s0 + 16 * (e >> 3) + 8 * half + (e & 7);
+            if (key >= nk || (CAUSAL && key > qlim)) s[blk][e] = kNegInf;
+          }
         }
+      }
+    }
+    if (alibi) {
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk) {
+        const float base = alibi_raw * (float)(s0 + 8 * half - (qw + 32 * blk + l32 + off));
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[blk][e] += fmaf(alibi_raw, (float)(16 * (e >> 3) + (e & 7)), base);
       }
     }
     float psum[NB];
@@ -597,7 +639,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // step 4t+1: softmax of subtile 2t; K of 2t+1
     fetch_half(fetch, 0);
     load_k(stg, 1);
-    softmax(64 * t);
+    softmax(key0 + 64 * t);
     if (!LAST) wait_tile(t + 1);
     pin_vector_step();
     step_end<true>();
@@ -609,7 +651,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // step 4t+3: softmax of 2t+1; K of 2t+2
     fetch_half(fetch, 1);
     if (!LAST) load_k(next_stage(stg), 0);
-    softmax(64 * t + 32);
+    softmax(key0 + 64 * t + 32);
     pin_vector_step();
     step_end<true>();
     // step 4t+4: scores of 2t+2, P·V of 2t+1; V of 2t+2
@@ -646,46 +688,48 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 template <class T, int D, bool CAUSAL, bool VARLEN>
 static hipError_t launch_prefill_t(const void* q, const void* k, const void* v, void* o, int batch, int hq, int hkv,
-                                   int n, float scale, VarlenArgs vl, hipStream_t stream) {
+                                   int n, float scale, VarlenArgs vl, MaskArgs mk, hipStream_t stream) {
   using Cfg = PrefillCfg<D>;
   const int tiles = (n + Cfg::BR - 1) / Cfg::BR;
   // varlen: 8 XCDs x (units of the fullest XCD) x query heads per unit x tiles
   const long long blocks = VARLEN ? 8LL * ((batch * hkv + 7) / 8) * (hq / hkv) * tiles : (long long)tiles * hq * batch;
   prefill_fwd_kernel<T, D, CAUSAL, VARLEN><<<dim3((unsigned)blocks), dim3(64 * Cfg::WAVES), 0, stream>>>(
       static_cast<const char*>(q), static_cast<const char*>(k), static_cast<const char*>(v), static_cast<char*>(o),
-      batch, hq, hkv, n, scale * kLog2e, tiles, vl);
+      batch, hq, hkv, n, scale * kLog2e, tiles, vl, mk);
   return hipGetLastError();
 }
 
 template <class T, int D, bool VARLEN>
 static hipError_t launch_prefill_d(const void* q, const void* k, const void* v, void* o, int batch, int hq, int hkv,
-                                   int n, float scale, bool causal, VarlenArgs vl, hipStream_t stream) {
-  return causal ? launch_prefill_t<T, D, true, VARLEN>(q, k, v, o, batch, hq, hkv, n, scale, vl, stream)
-                : launch_prefill_t<T, D, false, VARLEN>(q, k, v, o, batch, hq, hkv, n, scale, vl, stream);
+                                   int n, float scale, bool causal, VarlenArgs vl, MaskArgs mk, hipStream_t stream) {
+  return causal ? launch_prefill_t<T, D, true, VARLEN>(q, k, v, o, batch, hq, hkv, n, scale, vl, mk, stream)
+                : launch_prefill_t<T, D, false, VARLEN>(q, k, v, o, batch, hq, hkv, n, scale, vl, mk, stream);
 }
 
 template <bool VARLEN>
 static hipError_t launch_prefill_any(const void* q, const void* k, const void* v, void* o, bool bf16, int batch,
                                      int hq, int hkv, int n, int d, float scale, bool causal, VarlenArgs vl,
-                                     hipStream_t stream) {
+                                     MaskArgs mk, hipStream_t stream) {
   if (bf16)
-    return d == 64 ? launch_prefill_d<Bf16, 64, VARLEN>(q, k, v, o, batch, hq, hkv, n, scale, causal, vl, stream)
-                   : launch_prefill_d<Bf16, 128, VARLEN>(q, k, v, o, batch, hq, hkv, n, scale, causal, vl, stream);
-  return d == 64 ? launch_prefill_d<F16, 64, VARLEN>(q, k, v, o, batch, hq, hkv, n, scale, causal, vl, stream)
-                 : launch_prefill_d<F16, 128, VARLEN>(q, k, v, o, batch, hq, hkv, n, scale, causal, vl, stream);
+    return d == 64
+               ? launch_prefill_d<Bf16, 64, VARLEN>(q, k, v, o, batch, hq, hkv, n, scale, causal, vl, mk, stream)
+               : launch_prefill_d<Bf16, 128, VARLEN>(q, k, v, o, batch, hq, hkv, n, scale, causal, vl, mk, stream);
+  return d == 64 ? launch_prefill_d<F16, 64, VARLEN>(q, k, v, o, batch, hq, hkv, n, scale, causal, vl, mk, stream)
+                 : launch_prefill_d<F16, 128, VARLEN>(q, k, v, o, batch, hq, hkv, n, scale, causal, vl, mk, stream);
 }
 
 hipError_t launch_prefill(const void* q, const void* k, const void* v, void* o, bool bf16, int batch, int hq,
                           int hkv, int n, int d, float scale, bool causal, hipStream_t stream) {
   return launch_prefill_any<false>(q, k, v, o, bf16, batch, hq, hkv, n, d, scale, causal,
-                                   VarlenArgs{nullptr, nullptr, 0, 0, 0}, stream);
+                                   VarlenArgs{nullptr, nullptr, 0, 0, 0}, MaskArgs{0, nullptr}, stream);
 }
 
 hipError_t launch_prefill_varlen(const void* q, const void* k, const void* v, void* o, const int* cu_q,
                                  const int* cu_k, int total_q, int total_k, int max_q, int max_k, bool bf16, int batch,
-                                 int hq, int hkv, int d, float scale, bool causal, hipStream_t stream) {
+                                 int hq, int hkv, int d, float scale, bool causal, int window, const float* alibi,
+                                 hipStream_t stream) {
   return launch_prefill_any<true>(q, k, v, o, bf16, batch, hq, hkv, max_q, d, scale, causal,
-                                  VarlenArgs{cu_q, cu_k, total_q, total_k, max_k}, stream);
+                                  VarlenArgs{cu_q, cu_k, total_q, total_k, max_k}, MaskArgs{window, alibi}, stream);
 }
 
 }  // namespace attn

@@ -106,6 +106,14 @@ attn_status attn_prefill_fwd(const void* q, const void* k, const void* v, void* 
  *   max_seqlen_q >= 1, max_seqlen_k >= 0 : bounds on nq and nk (the grid is
  *          sized from max_seqlen_q)
  *   scale, causal : as for attn_prefill_fwd
+ *   window : 0 = no window; W > 0 = sliding window: query i (position
+ *          p = i + nk - nq) sees keys p - W < j <= p.  Needs `causal`
+ *          (else ATTN_ERR_UNSUPPORTED); negative is ATTN_ERR_BAD_SHAPE.
+ *   alibi_slopes : NULL = none; else [hq] fp32 in DEVICE memory: query head
+ *          h adds -alibi_slopes[h]·(p - j) to its score of key j (natural-log
+ *          units, after the scale).  Both masking variants are those of
+ *          "Masking variants", section 5 of "Attention Computation in
+ *          Practice".
  *
  * Limits: total·heads·d below 2^40 for each tensor; max_seqlen_k·hkv·d·2 below
  * 2^31 bytes (else ATTN_ERR_TOO_LARGE).  O must not alias Q, K or V.
@@ -113,7 +121,7 @@ attn_status attn_prefill_fwd(const void* q, const void* k, const void* v, void* 
 attn_status attn_prefill_varlen_fwd(const void* q, const void* k, const void* v, void* o, const int* cu_seqlens_q,
                                     const int* cu_seqlens_k, int total_q, int total_k, int max_seqlen_q,
                                     int max_seqlen_k, int dtype, int batch, int hq, int hkv, int d, float scale,
-                                    int causal, void* stream);
+                                    int causal, int window, const float* alibi_slopes, void* stream);
 
 /*
  * Split-K ("Flash-Decoding") single-query decode, in two calls: partial states

@@ -67,19 +67,27 @@ def kv_head_of(h: int, hq: int, hkv: int) -> int:
     return h // (hq // hkv)
 
 
-def _materialised_rows(q_rows, K, V, scale, row_index=None):
+def _materialised_rows(q_rows, K, V, scale, row_index=None, window: int = 0, bias=None):
     """Softmax attention of a block of query rows over keys ``K`` / values ``V``.
 
     The whole block of score rows is materialised (as the textbook version on
     "Attention Computation in Practice", section 4, does one row at a time),
-    masked, shifted by its row maximum, exponentiated, normalised by its row sum
-    and multiplied by V.  ``row_index`` gives each row's query position when the
-    causal mask applies, else ``None``.
+    offset by ``bias`` if given, masked, shifted by its row maximum,
+    exponentiated, normalised by its row sum and multiplied by V.  ``row_index``
+    gives each row's query position when the causal mask applies, else
+    ``None``; with ``window > 0`` a row at position p also drops keys
+    ``j <= p - window`` (sliding window, "Masking variants" in section 5).
     """
     S = scale * (q_rows @ K.T)
+    if bias is not None:
+        S = S + bias
     if row_index is not None:
-        j = np.arange(K.shape[0])
-        S = np.where(j[None, :] <= np.asarray(row_index)[:, None], S, -np.inf)
+        j = np.arange(K.shape[0])[None, :]
+        r = np.asarray(row_index)[:, None]
+        visible = j <= r
+        if window > 0:
+            visible = visible & (j > r - window)
+        S = np.where(visible, S, -np.inf)
     if S.shape[1] == 0:
         return np.zeros((q_rows.shape[0], V.shape[1]))
     m = S.max(axis=1, keepdims=True)
@@ -114,7 +122,8 @@ def attention(q, k, v, scale: float, causal: bool = False, row_block: int = 256)
     return out
 
 
-def attention_varlen(q, k, v, cu_q, cu_k, scale: float, causal: bool = False):
+def attention_varlen(q, k, v, cu_q, cu_k, scale: float, causal: bool = False, window: int = 0,
+                     alibi_slopes=None):
     """Exact attention over a packed batch of sequences of different lengths.
 
     ``q: [total_q, Hq, d]`` and ``k, v: [total_k, Hkv, d]`` (token-major);
@@ -125,8 +134,14 @@ def attention_varlen(q, k, v, cu_q, cu_k, scale: float, causal: bool = False):
     positions, so query ``i`` stands at position ``i + nk - nq`` and, under
     the causal rule ``j <= position`` ("Masking variants", same section),
     sees keys ``0 .. i + nk - nq``.  A query that sees no key gives 0.
-    Returns ``O: [total_q, Hq, d]`` in fp64 (rows owned by no sequence are 0).
+    ``window = W > 0`` (causal only) keeps keys ``p - W < j <= p`` for the
+    query at position ``p``; ``alibi_slopes`` (one slope ``m_h`` per query head)
+    adds ``-m_h·(p - j)`` to every score (both from "Masking variants", same
+    section).  Returns ``O: [total_q, Hq, d]`` in fp64 (rows owned by no
+    sequence are 0).
     """
+    if window and not causal:
+        raise ValueError("a sliding window is defined together with the causal mask")
     q, k, v = _f64(q), _f64(k), _f64(v)
     total_q, Hq, d = q.shape
     Hkv = k.shape[1]
@@ -136,10 +151,14 @@ def attention_varlen(q, k, v, cu_q, cu_k, scale: float, causal: bool = False):
         nq, nk = qe - qs, ke - ks
         if nq < 0 or nk < 0:
             raise ValueError(f"sequence {b}: offsets decrease")
-        positions = np.arange(nq) + (nk - nq) if causal else None
+        positions = np.arange(nq) + (nk - nq)
         for h in range(Hq):
             kh = kv_head_of(h, Hq, Hkv)
-            out[qs:qe, h] = _materialised_rows(q[qs:qe, h], k[ks:ke, kh], v[ks:ke, kh], scale, positions)
+            bias = None
+            if alibi_slopes is not None:
+                bias = -float(alibi_slopes[h]) * (positions[:, None] - np.arange(nk)[None, :])
+            out[qs:qe, h] = _materialised_rows(q[qs:qe, h], k[ks:ke, kh], v[ks:ke, kh], scale,
+                                               positions if causal else None, window, bias)
     return out
 
 

@@ -55,17 +55,17 @@ def test_prefill_rejects_bad_arguments(lib, kw, status):
 
 
 def varlen(lib, q=P, k=P, v=P, o=P, cq=P, ck=P, tq=100, tk=200, mq=50, mk=120, dtype=BF16, batch=2, hq=4, hkv=2,
-           d=128, scale=0.1, causal=1):
+           d=128, scale=0.1, causal=1, window=0, alibi=None):
     return lib.attn_prefill_varlen_fwd(q, k, v, o, cq, ck, tq, tk, mq, mk, dtype, batch, hq, hkv, d, scale, causal,
-                                       None)
+                                       window, alibi, None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), NULL), (dict(k=None), NULL), (dict(v=None), NULL), (dict(o=None), NULL), (dict(cq=None), NULL),
     (dict(ck=None), NULL),
     (dict(batch=0), SHAPE), (dict(tq=0), SHAPE), (dict(tk=-1), SHAPE), (dict(mq=0), SHAPE), (dict(mk=-1), SHAPE),
-    (dict(hq=3), SHAPE), (dict(scale=float("nan")), SHAPE),
-    (dict(d=32), UNSUP), (dict(dtype=2), UNSUP),
+    (dict(hq=3), SHAPE), (dict(scale=float("nan")), SHAPE), (dict(window=-1), SHAPE),
+    (dict(d=32), UNSUP), (dict(dtype=2), UNSUP), (dict(window=16, causal=0), UNSUP),
     (dict(q=P + 8), MISAL), (dict(o=P + 2), MISAL),
     (dict(mk=1 << 21, hkv=4, hq=4), BIG), (dict(tq=1 << 30, hq=64), BIG),
 ])

@@ -166,6 +166,45 @@ def test_varlen_equal_lengths_match_square_kernel_bitwise(A, d, causal):
     assert torch.equal(out, sq.transpose(1, 2).reshape(B * n, hq, d))
 
 
+def alibi_slopes(hq):
+    """The usual geometric ALiBi slopes 2^(-8(h+1)/hq), as fp32."""
+    return torch.tensor([2.0 ** (-8.0 * (h + 1) / hq) for h in range(hq)], dtype=torch.float32)
+
+
+@pytest.mark.parametrize("d,dtype", [(64, "bf16"), (128, "bf16"), (128, "f16")])
+@pytest.mark.parametrize("window", [1, 17, 64, 300, 5000])
+def test_varlen_sliding_window(A, window, d, dtype):
+    """Windows of 1 key, within a subtile, one tile, several tiles and wider
+    than every sequence, on mixed append lengths (nq < nk, nq = nk, nq > nk)."""
+    w = varlen_w(8, 2, d, True, dtype)
+    nq, nk = [1, 300, 700, 40, 513], [9, 1200, 700, 20, 2000]
+    announce(f"varlen window={window} d={d} {dtype}")
+    q, k, v, cu_q, cu_k = workloads.varlen_inputs(w, device=DEV, nq=nq, nk=nk)
+    out = A.prefill_varlen_fwd(q, k, v, cu_q.to(DEV), cu_k.to(DEV), max(nq), max(nk), causal=True, scale=w.scale,
+                               window=window)
+    torch.cuda.synchronize()
+    ref = oracle.attention_varlen(f64(q), f64(k), f64(v), cu_q.numpy(), cu_k.numpy(), w.scale, True, window=window)
+    assert_close(out, ref, f"varlen window={window}")
+
+
+@pytest.mark.parametrize("causal,window", [(True, 0), (False, 0), (True, 100)])
+@pytest.mark.parametrize("d", [64, 128])
+def test_varlen_alibi(A, causal, window, d):
+    """ALiBi slopes 2^(-8(h+1)/H) over 16 query heads (GQA 4), alone and with a
+    sliding window; non-causal ALiBi adds -m·(p - j) for keys after p too."""
+    w = varlen_w(16, 4, d, causal, "bf16")
+    nq, nk = [1, 300, 257, 64], [700, 1200, 257, 64]
+    announce(f"varlen alibi causal={causal} window={window} d={d}")
+    q, k, v, cu_q, cu_k = workloads.varlen_inputs(w, device=DEV, nq=nq, nk=nk)
+    sl = alibi_slopes(16)
+    out = A.prefill_varlen_fwd(q, k, v, cu_q.to(DEV), cu_k.to(DEV), max(nq), max(nk), causal=causal,
+                               scale=w.scale, window=window, alibi_slopes=sl.to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle.attention_varlen(f64(q), f64(k), f64(v), cu_q.numpy(), cu_k.numpy(), w.scale, causal,
+                                  window=window, alibi_slopes=sl.double().numpy())
+    assert_close(out, ref, f"varlen alibi causal={causal} window={window}")
+
+
 def test_varlen_clamps_offsets_into_the_tensors(A):
     """Offsets past the packed tensors are clamped to their ends, and a
     sequence longer than max_seqlen_k to its first max_seqlen_k keys: the

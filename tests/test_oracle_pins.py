@@ -393,6 +393,66 @@ def test_varlen_matches_sdpa_with_bottom_right_mask():
         assert np.max(np.abs(out[cu_q[b]:cu_q[b + 1]] - ref.numpy().transpose(1, 0, 2))) <= TOL
 
 
+def test_sliding_window_with_zero_queries_is_a_moving_average():
+    """Q = 0 makes every visible key equally likely, so the output at position
+    p is the mean of V over (p - W, p] (computed here with running sums)."""
+    n, d, W = 40, 3, 7
+    v = gauss(122, n, 1, d)
+    k = gauss(123, n, 1, d)
+    out = oracle.attention_varlen(np.zeros((n, 1, d)), k, v, [0, n], [0, n], 0.5, True, window=W)[:, 0]
+    csum = np.concatenate([np.zeros((1, d)), np.cumsum(v[:, 0], axis=0)])
+    for p_ in range(n):
+        lo = max(0, p_ - W + 1)
+        assert np.max(np.abs(out[p_] - (csum[p_ + 1] - csum[lo]) / (p_ + 1 - lo))) <= TOL
+
+
+def test_window_covering_every_key_changes_nothing_bit_exact():
+    q, k, v = gauss(124, 9, 2, 8), gauss(125, 30, 1, 8), gauss(126, 30, 1, 8)
+    a = oracle.attention_varlen(q, k, v, [0, 9], [0, 30], 0.3, True)
+    assert np.array_equal(oracle.attention_varlen(q, k, v, [0, 9], [0, 30], 0.3, True, window=30), a)
+    assert np.array_equal(oracle.attention_varlen(q, k, v, [0, 9], [0, 30], 0.3, True, window=10 ** 6), a)
+    assert not np.array_equal(oracle.attention_varlen(q, k, v, [0, 9], [0, 30], 0.3, True, window=29), a)
+    with pytest.raises(ValueError):
+        oracle.attention_varlen(q, k, v, [0, 9], [0, 30], 0.3, False, window=4)
+
+
+def test_alibi_with_zero_queries_is_a_geometric_average():
+    """Q = 0 and slope m: key j at distance p - j gets weight r^(p-j), r = e^-m;
+    the weighted mean is summed here term by term."""
+    n, d = 25, 2
+    m = np.array([0.3, 1.1])
+    v = gauss(127, n, 1, d)
+    out = oracle.attention_varlen(np.zeros((n, 2, d)), gauss(128, n, 1, d), v, [0, n], [0, n], 0.25, True,
+                                  alibi_slopes=m)
+    for h in range(2):
+        r = math.exp(-m[h])
+        for p_ in range(n):
+            num = sum(r ** (p_ - j) * v[j, 0] for j in range(p_ + 1))
+            den = sum(r ** (p_ - j) for j in range(p_ + 1))
+            assert np.max(np.abs(out[p_, h] - num / den)) <= TOL
+
+
+def test_alibi_slope_zero_is_plain_attention_bit_exact_and_matches_sdpa():
+    hq, d, nq, nk = 4, 8, 6, 20
+    q, k, v = gauss(129, nq, hq, d), gauss(130, nk, 2, d), gauss(131, nk, 2, d)
+    plain = oracle.attention_varlen(q, k, v, [0, nq], [0, nk], 0.4, True)
+    assert np.array_equal(oracle.attention_varlen(q, k, v, [0, nq], [0, nk], 0.4, True,
+                                                  alibi_slopes=np.zeros(hq)), plain)
+    slopes = np.array([0.5, 0.25, 0.125, 0.0625])
+    got = oracle.attention_varlen(q, k, v, [0, nq], [0, nk], 0.4, True, window=9, alibi_slopes=slopes)
+    for h in range(hq):
+        bias = np.full((nq, nk), -np.inf)
+        for i in range(nq):
+            p_ = i + nk - nq
+            for j in range(nk):
+                if p_ - 9 < j <= p_:
+                    bias[i, j] = -slopes[h] * (p_ - j)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[:, h][None]), torch.from_numpy(k[:, h // 2][None]),
+            torch.from_numpy(v[:, h // 2][None]), attn_mask=torch.from_numpy(bias), scale=0.4)[0]
+        assert np.max(np.abs(got[:, h] - ref.numpy())) <= TOL
+
+
 def test_varlen_visible_pair_count():
     w = workloads.Varlen("t", 3, 1, 1, 64, True, "bf16", (1, 1), (0, 0))
     # nq=nk=4: 1+2+3+4; nq=2 of nk=5: 4+5; nq=5 of nk=3: 0+0+1+2+3
