@@ -153,9 +153,10 @@ def decode_splitk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
 
 def decode_splitk_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, block_table: torch.Tensor,
                         kv_lens: torch.Tensor, num_splits: Optional[int] = None, scale: Optional[float] = None,
-                        partials=None):
+                        partials=None, window: int = 0, alibi_slopes: Optional[torch.Tensor] = None):
     """Partial states over a paged cache: ``k_pages, v_pages: [P, Hkv, page, d]``,
-    ``block_table: [B, max_pages]`` int32 (device).  Same outputs as ``decode_splitk``."""
+    ``block_table: [B, max_pages]`` int32 (device).  Same outputs as ``decode_splitk``; ``window > 0`` keeps
+    only the last ``window`` keys, ``alibi_slopes`` (fp32 device ``[Hq]``) adds ``-slope·(p - j)``."""
     lib = _lib_handle()
     if q.dim() != 3 or k_pages.dim() != 4 or v_pages.shape != k_pages.shape or block_table.dim() != 2:
         raise ValueError("expected q [B, Hq, d], pages [P, Hkv, page, d] and block_table [B, max_pages]")
@@ -167,6 +168,9 @@ def decode_splitk_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.T
         raise ValueError("block_table must be an int32 device tensor [B, max_pages]")
     if kv_lens.dtype != torch.int32 or kv_lens.numel() != B or kv_lens.device != q.device:
         raise ValueError("kv_lens must be an int32 device tensor with one entry per sequence")
+    if alibi_slopes is not None and (alibi_slopes.dtype != torch.float32 or alibi_slopes.numel() != hq
+                                     or alibi_slopes.device != q.device):
+        raise ValueError("alibi_slopes must be a float32 device tensor with one slope per query head")
     max_pages = block_table.shape[1]
     S = decode_num_splits(B, hkv, max_pages * page) if num_splits is None else int(num_splits)
     if partials is None:
@@ -178,6 +182,7 @@ def decode_splitk_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.T
     st = lib.attn_decode_splitk_paged(_dev(q, "q"), _dev(k_pages, "k_pages"), _dev(v_pages, "v_pages"),
                                       _dev(block_table, "block_table"), max_pages, P, page,
                                       _dev(kv_lens, "kv_lens"), _dtype_code(q), B, hq, hkv, d, _scale(scale, d), S,
+                                      int(window), None if alibi_slopes is None else _dev(alibi_slopes, "alibi"),
                                       _dev(pm, "part_m"), _dev(pl, "part_l"), _dev(po, "part_o"), _stream(q))
     _lib.check("attn_decode_splitk_paged", st)
     return pm, pl, po
@@ -209,7 +214,8 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_len
 
 def decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, block_table: torch.Tensor,
                  kv_lens: torch.Tensor, num_splits: Optional[int] = None, scale: Optional[float] = None,
-                 partials=None) -> torch.Tensor:
+                 partials=None, window: int = 0, alibi_slopes: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Single-query decode over a paged cache: paged split-K partials then their merge."""
-    pm, pl, po = decode_splitk_paged(q, k_pages, v_pages, block_table, kv_lens, num_splits, scale, partials)
+    pm, pl, po = decode_splitk_paged(q, k_pages, v_pages, block_table, kv_lens, num_splits, scale, partials,
+                                     window, alibi_slopes)
     return merge_partials(pm, pl, po, q.dtype)

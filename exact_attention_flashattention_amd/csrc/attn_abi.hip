@@ -138,11 +138,12 @@ attn_status attn_decode_splitk(const void* q, const void* k_cache, const void* v
 attn_status attn_decode_splitk_paged(const void* q, const void* k_pages, const void* v_pages, const int* block_table,
                                      int max_pages_per_seq, int num_pages, int page_size, const int* kv_lens,
                                      int dtype, int batch, int hq, int hkv, int d, float scale, int num_splits,
-                                     float* part_m, float* part_l, float* part_o, void* stream) {
+                                     int window, const float* alibi_slopes, float* part_m, float* part_l,
+                                     float* part_o, void* stream) {
   if (!q || !k_pages || !v_pages || !block_table || !kv_lens || !part_m || !part_l || !part_o)
     return ATTN_ERR_NULL_PTR;
   if (batch < 1 || hq < 1 || hkv < 1 || max_pages_per_seq < 1 || num_pages < 1 || num_splits < 1 ||
-      hq % hkv != 0 || !scale_ok(scale))
+      hq % hkv != 0 || !scale_ok(scale) || window < 0)
     return ATTN_ERR_BAD_SHAPE;
   if (page_size < 16 || (page_size & (page_size - 1)) != 0) return ATTN_ERR_UNSUPPORTED;
   if ((d != 64 && d != 128) || !dtype_ok(dtype)) return ATTN_ERR_UNSUPPORTED;
@@ -158,7 +159,7 @@ attn_status attn_decode_splitk_paged(const void* q, const void* k_pages, const v
   const int chunk = attn_decode_chunk_len((int)max_kv_len, num_splits);
   return from_hip(attn::launch_decode_splitk_paged(q, k_pages, v_pages, block_table, max_pages_per_seq, num_pages,
                                                    shift, kv_lens, dtype == ATTN_BF16, batch, hq, hkv, d, scale,
-                                                   num_splits, chunk, part_m, part_l, part_o,
+                                                   num_splits, chunk, window, alibi_slopes, part_m, part_l, part_o,
                                                    static_cast<hipStream_t>(stream)));
 }
 

@@ -35,6 +35,13 @@
 // pages sit one per lane in a VGPR (one vector load, refreshed when a split
 // runs past them) and are picked out with v_readlane, so the gather adds no
 // memory round trip to a step.
+//
+// The paged kernel also takes the masking variants of "Masking variants"
+// (same section), for the query at position p = kv_len - 1: a sliding window
+// W keeps keys p - W < j <= p (splits wholly before the window are empty, the
+// others start at the first 32-key step the window reaches), and ALiBi adds
+// -m_h·(p - j) to every score of query head h, folded into the raw scores as
+// (m_h / scale)·(j - p).
 #include "device_common.hpp"
 #include "launchers.hpp"
 
@@ -62,11 +69,18 @@ struct PageTable {
   int shift;         // log2 of the page size
 };
 
+// Masking variants of the paged kernel (zero / null: none).
+struct DecodeMask {
+  int window;          // > 0: only the last `window` keys are visible
+  const float* alibi;  // [hq] ALiBi slopes, natural-log units per position
+};
+
 template <class T, int D, bool PAGED>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void decode_splitk_kernel(
     const char* __restrict__ q, const char* __restrict__ kc, const char* __restrict__ vc,
     const int* __restrict__ kv_lens, int max_kv_len, int hq, int hkv, int g, int chunk, int num_splits, float c,
-    float* __restrict__ part_m, float* __restrict__ part_l, float* __restrict__ part_o, PageTable pt) {
+    float* __restrict__ part_m, float* __restrict__ part_l, float* __restrict__ part_o, PageTable pt,
+    DecodeMask mk) {
   constexpr int KK = D / 32;
   constexpr int DT = D / 16;              // 16-row output tiles of the head dimension
   constexpr int VCH = D / 16;
@@ -87,8 +101,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 
   int kv_len = kv_lens[b];
   kv_len = kv_len < 0 ? 0 : (kv_len > max_kv_len ? max_kv_len : kv_len);
-  const int start = split * chunk;
-  const int end = min(start + chunk, kv_len);
+  // first visible key: 0, or the window's first key; a split starts at the
+  // first 32-key step that holds a visible key
+  const int lo = (PAGED && mk.window > 0) ? max(0, kv_len - mk.window) : 0;
+  const int start = max(split * chunk, lo & ~(kStep - 1));
+  const int end = min(split * chunk + chunk, kv_len);
 
   const size_t prow = ((size_t)b * hq + h) * num_splits + split;
   float* po = part_o + prow * D;
@@ -183,6 +200,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     }
   };
 
+  // ALiBi slope of this lane's query head in raw-score units (scores are scaled by c = scale·log2 e later)
+  const float alibi_raw = (PAGED && mk.alibi != nullptr && qvalid) ? mk.alibi[h] * kLog2e / c : 0.f;
+  const bool alibi = PAGED && mk.alibi != nullptr;
+
   float m_run = kNegInf, l_run = 0.f;
   f32x4 oacc[DT];
 #pragma unroll
@@ -203,17 +224,27 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) s[sb] = T::mfma16(st.k[sb][kk], qf[kk], s[sb]);
     }
-    if (k0 + kStep > end) {
+    if (alibi) {  // + (m/scale)·(j - p) for key j = k0 + 16·sb + 4·grp + e, p = kv_len - 1
+      const float base = alibi_raw * (float)(k0 + 4 * grp - (kv_len - 1));
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (k0 + sb * 16 + 4 * grp + e >= end) s[sb][e] = kNegInf;
+        for (int e = 0; e < 4; ++e) s[sb][e] += fmaf(alibi_raw, (float)(16 * sb + e), base);
+    }
+    if (k0 + kStep > end || k0 < lo) {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = k0 + sb * 16 + 4 * grp + e;
+          if (key >= end || key < lo) s[sb][e] = kNegInf;
+        }
     }
     float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                      fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
     mx = max_xor32(max_xor16(mx));
-    // every processed step holds at least one live key, so m_new is finite
+    // every processed step holds at least one live key (a split starts at or
+    // after the step holding lo), so m_new is finite
     const float m_new = fmaxf(m_run, mx * c);
     const float alpha = fast_exp2(m_run - m_new);  // 0 on the first step (m_run = -inf)
     float psum = 0.f;
@@ -269,13 +300,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 template <class T, int D, bool PAGED>
 static hipError_t launch_decode_t(const void* q, const void* kc, const void* vc, const int* kv_lens, int max_kv_len,
                                   int batch, int hq, int hkv, float scale, int num_splits, int chunk, float* pm,
-                                  float* pl, float* po, PageTable pt, hipStream_t stream) {
+                                  float* pl, float* po, PageTable pt, DecodeMask mk, hipStream_t stream) {
   const int g = hq / hkv;
   const int groups = (g + 15) / 16;
   dim3 grid(num_splits, hkv * groups, batch);
   decode_splitk_kernel<T, D, PAGED><<<grid, dim3(64), 0, stream>>>(
       static_cast<const char*>(q), static_cast<const char*>(kc), static_cast<const char*>(vc), kv_lens, max_kv_len,
-      hq, hkv, g, chunk, num_splits, scale * kLog2e, pm, pl, po, pt);
+      hq, hkv, g, chunk, num_splits, scale * kLog2e, pm, pl, po, pt, mk);
   return hipGetLastError();
 }
 
@@ -283,17 +314,17 @@ template <bool PAGED>
 static hipError_t launch_decode_any(const void* q, const void* kc, const void* vc, const int* kv_lens,
                                     int max_kv_len, bool bf16, int batch, int hq, int hkv, int d, float scale,
                                     int num_splits, int chunk, float* pm, float* pl, float* po, PageTable pt,
-                                    hipStream_t stream) {
+                                    DecodeMask mk, hipStream_t stream) {
   if (bf16) {
     return d == 64 ? launch_decode_t<Bf16, 64, PAGED>(q, kc, vc, kv_lens, max_kv_len, batch, hq, hkv, scale,
-                                                      num_splits, chunk, pm, pl, po, pt, stream)
+                                                      num_splits, chunk, pm, pl, po, pt, mk, stream)
                    : launch_decode_t<Bf16, 128, PAGED>(q, kc, vc, kv_lens, max_kv_len, batch, hq, hkv, scale,
-                                                       num_splits, chunk, pm, pl, po, pt, stream);
+                                                       num_splits, chunk, pm, pl, po, pt, mk, stream);
   }
   return d == 64 ? launch_decode_t<F16, 64, PAGED>(q, kc, vc, kv_lens, max_kv_len, batch, hq, hkv, scale,
-                                                   num_splits, chunk, pm, pl, po, pt, stream)
+                                                   num_splits, chunk, pm, pl, po, pt, mk, stream)
                  : launch_decode_t<F16, 128, PAGED>(q, kc, vc, kv_lens, max_kv_len, batch, hq, hkv, scale,
-                                                    num_splits, chunk, pm, pl, po, pt, stream);
+                                                    num_splits, chunk, pm, pl, po, pt, mk, stream);
 }
 
 hipError_t launch_decode_splitk(const void* q, const void* k_cache, const void* v_cache, const int* kv_lens,
@@ -301,17 +332,19 @@ hipError_t launch_decode_splitk(const void* q, const void* k_cache, const void* 
                                 int num_splits, int chunk, float* part_m, float* part_l, float* part_o,
                                 hipStream_t stream) {
   return launch_decode_any<false>(q, k_cache, v_cache, kv_lens, max_kv_len, bf16, batch, hq, hkv, d, scale,
-                                  num_splits, chunk, part_m, part_l, part_o, PageTable{nullptr, 0, 0, 0}, stream);
+                                  num_splits, chunk, part_m, part_l, part_o, PageTable{nullptr, 0, 0, 0},
+                                  DecodeMask{0, nullptr}, stream);
 }
 
 hipError_t launch_decode_splitk_paged(const void* q, const void* k_pages, const void* v_pages,
                                       const int* block_table, int max_pages, int num_pages, int page_shift,
                                       const int* kv_lens, bool bf16, int batch, int hq, int hkv, int d, float scale,
-                                      int num_splits, int chunk, float* part_m, float* part_l, float* part_o,
-                                      hipStream_t stream) {
+                                      int num_splits, int chunk, int window, const float* alibi, float* part_m,
+                                      float* part_l, float* part_o, hipStream_t stream) {
   return launch_decode_any<true>(q, k_pages, v_pages, kv_lens, max_pages << page_shift, bf16, batch, hq, hkv, d,
                                  scale, num_splits, chunk, part_m, part_l, part_o,
-                                 PageTable{block_table, max_pages, num_pages, page_shift}, stream);
+                                 PageTable{block_table, max_pages, num_pages, page_shift}, DecodeMask{window, alibi},
+                                 stream);
 }
 
 }  // namespace attn

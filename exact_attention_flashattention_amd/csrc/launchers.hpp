@@ -23,12 +23,13 @@ hipError_t launch_decode_splitk(const void* q, const void* k_cache, const void* 
                                 hipStream_t stream);
 
 // Paged caches [num_pages, hkv, 1 << page_shift, d]; row j of sequence b is
-// row j % page of page block_table[b * max_pages + j / page].
+// row j % page of page block_table[b * max_pages + j / page].  window > 0 and
+// alibi (per query head slopes, or null) are the masking variants.
 hipError_t launch_decode_splitk_paged(const void* q, const void* k_pages, const void* v_pages,
                                       const int* block_table, int max_pages, int num_pages, int page_shift,
                                       const int* kv_lens, bool bf16, int batch, int hq, int hkv, int d, float scale,
-                                      int num_splits, int chunk, float* part_m, float* part_l, float* part_o,
-                                      hipStream_t stream);
+                                      int num_splits, int chunk, int window, const float* alibi, float* part_m,
+                                      float* part_l, float* part_o, hipStream_t stream);
 
 hipError_t launch_merge(const float* part_m, const float* part_l, const float* part_o, int rows, int d,
                         int num_splits, bool bf16, void* out, hipStream_t stream);

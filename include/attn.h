@@ -185,7 +185,8 @@ attn_status attn_decode_splitk(const void* q, const void* k_cache, const void* v
  * block_table[b·max_pages_per_seq + j / page_size].  Partials, splits and
  * units are exactly those of attn_decode_splitk with
  * max_kv_len = max_pages_per_seq · page_size, so the same merge applies and,
- * for the same logical cache contents, the partials are bit-identical.
+ * for the same logical cache contents and no masking variant, the partials
+ * are bit-identical.  With a window, splits wholly before it are empty.
  *
  *   q           : [batch, hq, d]                        elements of `dtype`
  *   k_pages     : [num_pages, hkv, page_size, d]        elements of `dtype`
@@ -199,6 +200,14 @@ attn_status attn_decode_splitk(const void* q, const void* k_cache, const void* v
  *                 0 .. kv_lens[b]-1, clamped into [0, max_pages_per_seq ·
  *                 page_size]; rows at or past it are never read.
  *   page_size   : a power of two >= 16 (else ATTN_ERR_UNSUPPORTED)
+ *   window      : 0 = every key; W > 0 = sliding window: the query, at
+ *                 position p = kv_lens[b] - 1, sees keys p - W < j <= p
+ *                 (negative: ATTN_ERR_BAD_SHAPE)
+ *   alibi_slopes: NULL = none; else [hq] fp32 in DEVICE memory: head h adds
+ *                 -alibi_slopes[h]·(p - j) to its score of key j (natural-log
+ *                 units, after the scale).  Both are the masking variants of
+ *                 "Masking variants", section 5 of "Attention Computation in
+ *                 Practice".
  *   part_m, part_l, part_o, num_splits : as for attn_decode_splitk
  *
  * Limits: max_pages_per_seq · page_size below 2^31 / d;
@@ -207,7 +216,8 @@ attn_status attn_decode_splitk(const void* q, const void* k_cache, const void* v
 attn_status attn_decode_splitk_paged(const void* q, const void* k_pages, const void* v_pages,
                                      const int* block_table, int max_pages_per_seq, int num_pages, int page_size,
                                      const int* kv_lens, int dtype, int batch, int hq, int hkv, int d, float scale,
-                                     int num_splits, float* part_m, float* part_l, float* part_o, void* stream);
+                                     int num_splits, int window, const float* alibi_slopes, float* part_m,
+                                     float* part_l, float* part_o, void* stream);
 
 /*
  * attn_merge_partials -- merge the partial states of each (sequence, head)

@@ -233,14 +233,17 @@ def gather_pages(pages, table_row, length: int, kv_head: int):
     return rows
 
 
-def decode_paged(q, k_pages, v_pages, block_table, kv_lens, scale: float):
+def decode_paged(q, k_pages, v_pages, block_table, kv_lens, scale: float, window: int = 0, alibi_slopes=None):
     """Single-query attention over a paged KV cache.
 
     ``q: [B, Hq, d]``, ``k_pages, v_pages: [P, Hkv, page_size, d]``,
     ``block_table: [B, max_pages]``, ``kv_lens: [B]``.  The gather of
     ``gather_pages`` followed by the same attention as ``decode``: the pages
-    change where rows live, not what is computed.  Returns ``O: [B, Hq, d]``
-    in fp64.
+    change where rows live, not what is computed.  The query stands at
+    position ``p = kv_len - 1``; ``window = W > 0`` keeps keys
+    ``p - W < j <= p`` and ``alibi_slopes`` adds ``-m_h·(p - j)`` to the
+    scores of head ``h`` ("Masking variants", same section).  Returns
+    ``O: [B, Hq, d]`` in fp64.
     """
     q = _f64(q)
     B, Hq, d = q.shape
@@ -256,7 +259,12 @@ def decode_paged(q, k_pages, v_pages, block_table, kv_lens, scale: float):
         for kh in range(Hkv):
             K = _f64(gather_pages(k_pages, block_table[b], L, kh))
             V = _f64(gather_pages(v_pages, block_table[b], L, kh))
-            out[b, kh * g:(kh + 1) * g] = _materialised_rows(q[b, kh * g:(kh + 1) * g], K, V, scale)
+            heads = np.arange(kh * g, (kh + 1) * g)
+            bias = None
+            if alibi_slopes is not None:
+                slopes = np.asarray([float(alibi_slopes[h]) for h in heads])
+                bias = -slopes[:, None] * ((L - 1) - np.arange(L))[None, :]
+            out[b, heads] = _materialised_rows(q[b, heads], K, V, scale, [L - 1] * g, window, bias)
     return out
 
 

@@ -91,16 +91,16 @@ def test_decode_rejects_bad_arguments(lib, kw, status):
 
 
 def decode_paged(lib, q=P, kp=P, vp=P, table=P, max_pages=8, num_pages=20, ps=16, lens=P, dtype=BF16, batch=2,
-                 hq=4, hkv=2, d=128, scale=0.1, S=2, pm=P, pl=P, po=P):
+                 hq=4, hkv=2, d=128, scale=0.1, S=2, window=0, alibi=None, pm=P, pl=P, po=P):
     return lib.attn_decode_splitk_paged(q, kp, vp, table, max_pages, num_pages, ps, lens, dtype, batch, hq, hkv, d,
-                                        scale, S, pm, pl, po, None)
+                                        scale, S, window, alibi, pm, pl, po, None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), NULL), (dict(kp=None), NULL), (dict(vp=None), NULL), (dict(table=None), NULL),
     (dict(lens=None), NULL), (dict(pm=None), NULL), (dict(pl=None), NULL), (dict(po=None), NULL),
     (dict(max_pages=0), SHAPE), (dict(num_pages=0), SHAPE), (dict(S=0), SHAPE), (dict(batch=0), SHAPE),
-    (dict(hq=3), SHAPE), (dict(scale=float("inf")), SHAPE),
+    (dict(hq=3), SHAPE), (dict(scale=float("inf")), SHAPE), (dict(window=-2), SHAPE),
     (dict(ps=8), UNSUP), (dict(ps=24), UNSUP), (dict(ps=0), UNSUP), (dict(ps=-16), UNSUP), (dict(d=96), UNSUP),
     (dict(dtype=3), UNSUP),
     (dict(q=P + 2), MISAL), (dict(kp=P + 8), MISAL), (dict(vp=P + 4), MISAL), (dict(po=P + 4), MISAL),

@@ -478,6 +478,29 @@ def test_decode_paged_clamps_out_of_range_page_ids(A):
     assert_close(out, ref, "paged clamp")
 
 
+@pytest.mark.parametrize("window", [0, 1, 31, 32, 100, 3000])
+@pytest.mark.parametrize("alibi", [False, True])
+def test_decode_paged_window_and_alibi(A, window, alibi):
+    """Sliding windows of 1 key, just under / at a 32-key step, across steps,
+    and wider than the split size, with and without ALiBi slopes, on ragged
+    lengths; the heuristic split count and 3 splits."""
+    if window == 0 and not alibi:
+        pytest.skip("the plain case is covered above")
+    w = DEC
+    lens = torch.tensor([1, 17, 700, 2048, 1500], dtype=torch.int32)
+    q, kc, vc, lens = workloads.decode_inputs(w, device=DEV, kv_lens=lens, max_kv_len=2048, batch=5)
+    kp, vp, table = workloads.paged_from_cache(kc, vc, lens, 16, workloads.seed_for(w.name, "pages", 3))
+    sl = alibi_slopes(w.hq) if alibi else None
+    for S in (None, 3):
+        announce(f"paged window={window} alibi={alibi} S={S}")
+        out = A.decode_paged(q, kp, vp, table.to(DEV), lens.to(DEV), S, w.scale, window=window,
+                             alibi_slopes=None if sl is None else sl.to(DEV))
+        torch.cuda.synchronize()
+        ref = oracle.decode_paged(f64(q), f64(kp), f64(vp), table.numpy(), lens.numpy(), w.scale, window,
+                                  None if sl is None else sl.double().numpy())
+        assert_close(out, ref, f"paged window={window} alibi={alibi} S={S}")
+
+
 def test_decode_paged_long_context_full(A):
     """The 262144-key, 32/8-head cache as 16384 scattered 16-row pages (the
     benchmarked paged launch): partials bit-identical to the contiguous kernel's,

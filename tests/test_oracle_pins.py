@@ -545,6 +545,27 @@ def test_paged_decode_shared_pages_give_equal_outputs():
     assert not np.array_equal(out[0], out[2])
 
 
+@pytest.mark.parametrize("window,alibi", [(0, False), (5, False), (0, True), (12, True), (1, True)])
+def test_paged_decode_masks_equal_last_row_of_varlen(window, alibi):
+    """Decode with a window / ALiBi = the varlen oracle with one query per
+    sequence (standing at position kv_len - 1), which takes its masks from a
+    separately written path; slopes 2^-(h+1)."""
+    B, hq, hkv, L, d, ps = 3, 4, 2, 48, 8, 16
+    lens = [48, 1, 30]
+    q = gauss(132, B, hq, d)
+    kc, vc = gauss(133, B, hkv, L, d), gauss(134, B, hkv, L, d)
+    kp, table = contiguous_as_identity_pages(kc, ps)
+    vp, _ = contiguous_as_identity_pages(vc, ps)
+    slopes = 2.0 ** -(np.arange(hq) + 1.0) if alibi else None
+    got = oracle.decode_paged(q, kp, vp, table, lens, 0.3, window, slopes)
+    kpk = np.concatenate([kc[b, :, :n].transpose(1, 0, 2) for b, n in enumerate(lens)])
+    vpk = np.concatenate([vc[b, :, :n].transpose(1, 0, 2) for b, n in enumerate(lens)])
+    ref = oracle.attention_varlen(q, kpk, vpk, np.arange(B + 1), np.cumsum([0] + lens), 0.3, True, window, slopes)
+    assert np.max(np.abs(got - ref)) <= TOL
+    if window:
+        assert np.max(np.abs(got - oracle.decode_paged(q, kp, vp, table, lens, 0.3, 0, slopes))) > 1e-3
+
+
 def test_attention_rows_matches_full_output():
     B, hq, n, d = 1, 2, 130, 32
     q, k, v = gauss(62, B, hq, n, d), gauss(63, B, hq, n, d), gauss(64, B, hq, n, d)
