@@ -104,7 +104,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   // first visible key: 0, or the window's first key; a split starts at the
   // first 32-key step that holds a visible key
   const int lo = (PAGED && mk.window > 0) ? max(0, kv_len - mk.window) : 0;
-  const int start = max(split * chunk, lo & ~(kStep - 1));
+  const int start = PAGED ? max(split * chunk, lo & ~(kStep - 1)) : split * chunk;
   const int end = min(split * chunk + chunk, kv_len);
 
   const size_t prow = ((size_t)b * hq + h) * num_splits + split;
@@ -231,13 +231,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 #pragma unroll
         for (int e = 0; e < 4; ++e) s[sb][e] += fmaf(alibi_raw, (float)(16 * sb + e), base);
     }
-    if (k0 + kStep > end || k0 < lo) {
+    if (k0 + kStep > end || (PAGED && k0 < lo)) {
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int key = k0 + sb * 16 + 4 * grp + e;
-          if (key >= end || key < lo) s[sb][e] = kNegInf;
+          if (key >= end || (PAGED && key < lo)) s[sb][e] = kNegInf;
         }
     }
     float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
