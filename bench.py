@@ -25,9 +25,11 @@ After the step, the same decode is timed once more over a paged copy of the
 cache (16-row pages in a seeded random order, ``attn_decode_splitk_paged`` then
 ``attn_merge_partials``) in a region of its own, and so is a packed append
 batch (16 sequences of 256..2048 new queries on 0..16384 cached positions,
-causal, ``attn_prefill_varlen_fwd``).  Both are reported beside the step
-(``decode_paged``, ``append``, and in ``kernels``) and are not part of
-``value`` or ``ms_per_step``.
+causal, ``attn_prefill_varlen_fwd``), and the decode over the cache encoded
+as rotated 4-bit rows (``attn_decode_splitk_q4`` then ``attn_merge_partials``).
+They are reported beside the step (``decode_paged``, ``append``,
+``decode_q4`` and in ``kernels``) and are not part of ``value`` or
+``ms_per_step``.
 
 ``cpu_baseline`` times the fp64 oracle on a bounded sample of the same prefill
 workload (whole heads until about ``--cpu-seconds`` have passed), on the host
@@ -62,6 +64,7 @@ KERNEL_SOURCES = {
     "prefill_fwd_kernel": ["prefill_fwd.hip", "device_common.hpp"],
     "decode_splitk_kernel": ["decode_splitk.hip", "device_common.hpp"],
     "merge_partials_kernel": ["merge_partials.hip", "device_common.hpp"],
+    "decode_q4_kernel": ["decode_q4.hip", "device_common.hpp"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
@@ -144,7 +147,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "prefill_d64", "prefill_d128", "decode", "decode_paged", "append"], default="all",
+    ap.add_argument("--only", choices=["all", "prefill_d64", "prefill_d128", "decode", "decode_paged", "append", "decode_q4"], default="all",
                     help="run only one kernel family (for profiler runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of the bench, run plain device copies of this many MiB (counter calibration)")
@@ -181,6 +184,7 @@ def main() -> int:
     run_decode = args.only in ("all", "decode")
     run_paged = args.only in ("all", "decode_paged")
     run_append = args.only in ("all", "append")
+    run_q4 = args.only in ("all", "decode_q4")
 
     # ---- inputs (two copies each), outputs and workspaces: all allocated before timing
     pre = []
@@ -228,6 +232,19 @@ def main() -> int:
             copies.append((q, k, v, cu_q.to(dev), cu_k.to(dev)))
         outs = [torch.empty_like(c[0]) for c in copies]
         app = (w, copies, outs, nq, nk)
+    dq4 = None
+    if run_q4:
+        w = workloads.WORKLOADS[DECODE]
+        copies = []
+        for s in (0, 1):
+            q, kq, ks, vq, vs, lens = workloads.decode_q4_inputs(w, True, device=dev, salt=s)
+            copies.append((q, kq, ks, vq, vs, lens.to(dev)))
+        S = A.decode_num_splits(w.batch, w.hkv, w.max_kv_len)
+        part = (torch.empty((w.batch, w.hq, S), dtype=torch.float32, device=dev),
+                torch.empty((w.batch, w.hq, S), dtype=torch.float32, device=dev),
+                torch.empty((w.batch, w.hq, S, w.d), dtype=torch.float32, device=dev))
+        out = torch.empty((w.batch, w.hq, w.d), dtype=torch.bfloat16, device=dev)
+        dq4 = (w, copies, S, part, out, int(copies[0][5].sum()))
     torch.cuda.synchronize()
 
     def prefill_step(i, ev=None):
@@ -271,6 +288,18 @@ def main() -> int:
         A.prefill_varlen_fwd(q, k, v, cu_q, cu_k, max(nq), max(nk), causal=w.causal, scale=w.scale, out=outs[i % 2])
         if ev is not None:
             ev[1].record(stream)
+
+    def q4_step(i, ev=None):
+        w, copies, S, part, out, _ = dq4
+        q, kq, ks, vq, vs, lens = copies[i % 2]
+        if ev is not None:
+            ev[0].record(stream)
+        A.decode_splitk_q4(q, kq, ks, vq, vs, lens, True, S, w.scale, partials=part)
+        if ev is not None:
+            ev[1].record(stream)
+        A.merge_partials(*part, torch.bfloat16, out=out)
+        if ev is not None:
+            ev[2].record(stream)
 
     def events(n):
         return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
@@ -391,6 +420,35 @@ def main() -> int:
                        "queries": sum(nq), "keys": sum(nk),
                        "timed": "attn_prefill_varlen_fwd, wall clock, outside the step"}
 
+    # ---- 4-bit cache decode region (reported beside the step)
+    q4_line = None
+    if dq4:
+        w, copies, S, part, out, total_len = dq4
+        for i in range(W):
+            q4_step(i)
+        torch.cuda.synchronize()
+        ev = [events(3) for _ in range(K)]
+        t0 = time.perf_counter()
+        for i in range(K):
+            q4_step(i, ev[i])
+        torch.cuda.synchronize()
+        q4_wall = time.perf_counter() - t0
+        if not torch.isfinite(out).all():
+            raise RuntimeError("non-finite 4-bit decode output")
+        q4_bytes = 2.0 * w.hkv * total_len * (w.d // 2 + 4)  # codes + one fp32 scale per row, K and V
+        ms_split = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+        gbs = q4_bytes / (ms_split * 1e-3) / 1e9
+        label = "decode_q4_kernel<bf16,d128,rotated>"
+        result_kernels.append({
+            "kernel": label, "workload": f"{w.name} as rotated 4-bit rows", "avg_ms": ms_split, "bound": "hbm",
+            "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+            "traffic": measured_traffic(label, "decode_q4_kernel"), "algorithmic_bytes": q4_bytes,
+            "num_splits": S, "in_step": False})
+        q4_line = {"value": q4_bytes * K / q4_wall / 1e9, "unit": "GB/s",
+                   "frac_of_hbm_peak": q4_bytes * K / q4_wall / 1e9 / PEAK_HBM_GBS,
+                   "bf16_equivalent_gbs": w.kv_bytes(total_len) * K / q4_wall / 1e9,
+                   "timed": "attn_decode_splitk_q4 + attn_merge_partials, wall clock, outside the step"}
+
     dominant = max([r for r in result_kernels if r.get("in_step", True)] or result_kernels, key=lambda r: r["avg_ms"])
     roofline = {k: dominant[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
     roofline["kernel"] = dominant["kernel"]
@@ -422,6 +480,7 @@ def main() -> int:
                     "timed": "attn_decode_splitk + attn_merge_partials, wall clock"} if dec else None),
         "decode_paged": paged_line,
         "append": append_line,
+        "decode_q4": q4_line,
         "roofline": roofline,
         "kernels": result_kernels,
     }

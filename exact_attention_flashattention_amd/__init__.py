@@ -13,8 +13,10 @@ Entry points (same names as the C ABI):
 * ``decode_splitk(q, k_cache, v_cache, kv_lens, num_splits, scale)`` -- ``attn_decode_splitk``
 * ``decode_splitk_paged(q, k_pages, v_pages, block_table, kv_lens, num_splits, scale)`` --
   ``attn_decode_splitk_paged``
+* ``decode_splitk_q4(q, k_codes, k_scales, v_codes, v_scales, kv_lens, rotated, num_splits, scale)`` --
+  ``attn_decode_splitk_q4``
 * ``merge_partials(part_m, part_l, part_o, out_dtype)`` -- ``attn_merge_partials``
-* ``decode(...)``, ``decode_paged(...)`` -- split-K then merge, back to back on one stream
+* ``decode(...)``, ``decode_paged(...)``, ``decode_q4(...)`` -- split-K then merge, back to back on one stream
 * ``decode_num_splits``, ``decode_chunk_len``, ``decode_workspace_bytes`` -- host helpers
 """
 
@@ -28,7 +30,7 @@ import torch
 from . import _lib
 from ._lib import ATTN_BF16, ATTN_F16, AttnError  # noqa: F401
 
-__all__ = ["prefill_fwd", "prefill_varlen_fwd", "decode_splitk", "decode_splitk_paged", "merge_partials", "decode", "decode_paged",
+__all__ = ["prefill_fwd", "prefill_varlen_fwd", "decode_splitk", "decode_splitk_paged", "decode_splitk_q4", "decode_q4", "merge_partials", "decode", "decode_paged",
            "decode_num_splits", "decode_chunk_len", "decode_workspace_bytes", "AttnError"]
 
 _DTYPES = {torch.bfloat16: ATTN_BF16, torch.float16: ATTN_F16}
@@ -188,6 +190,38 @@ def decode_splitk_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.T
     return pm, pl, po
 
 
+def decode_splitk_q4(q: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Tensor, v_codes: torch.Tensor,
+                     v_scales: torch.Tensor, kv_lens: torch.Tensor, rotated: bool, num_splits: Optional[int] = None,
+                     scale: Optional[float] = None, partials=None):
+    """Partial states over a 4-bit cache: ``k_codes, v_codes: [B, Hkv, Lmax, d/2]`` uint8 (E2M1 pairs),
+    ``k_scales, v_scales: [B, Hkv, Lmax]`` fp32; ``rotated``: rows stored in the normalised Hadamard domain."""
+    lib = _lib_handle()
+    if q.dim() != 3 or k_codes.dim() != 4 or v_codes.shape != k_codes.shape:
+        raise ValueError("expected q [B, Hq, d] and code caches [B, Hkv, Lmax, d/2]")
+    B, hq, d = q.shape
+    _, hkv, L, half = k_codes.shape
+    if k_codes.shape[0] != B or 2 * half != d or k_codes.dtype != torch.uint8 or v_codes.dtype != torch.uint8:
+        raise ValueError("code caches must be uint8 [B, Hkv, Lmax, d/2]")
+    for name, t in (("k_scales", k_scales), ("v_scales", v_scales)):
+        if t.shape != (B, hkv, L) or t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32 [B, Hkv, Lmax]")
+    if kv_lens.dtype != torch.int32 or kv_lens.numel() != B or kv_lens.device != q.device:
+        raise ValueError("kv_lens must be an int32 device tensor with one entry per sequence")
+    S = decode_num_splits(B, hkv, L) if num_splits is None else int(num_splits)
+    if partials is None:
+        pm = torch.empty((B, hq, S), dtype=torch.float32, device=q.device)
+        pl = torch.empty((B, hq, S), dtype=torch.float32, device=q.device)
+        po = torch.empty((B, hq, S, d), dtype=torch.float32, device=q.device)
+    else:
+        pm, pl, po = partials
+    st = lib.attn_decode_splitk_q4(_dev(q, "q"), _dev(k_codes, "k_codes"), _dev(k_scales, "k_scales"),
+                                   _dev(v_codes, "v_codes"), _dev(v_scales, "v_scales"), _dev(kv_lens, "kv_lens"), L,
+                                   _dtype_code(q), B, hq, hkv, d, _scale(scale, d), int(bool(rotated)), S,
+                                   _dev(pm, "part_m"), _dev(pl, "part_l"), _dev(po, "part_o"), _stream(q))
+    _lib.check("attn_decode_splitk_q4", st)
+    return pm, pl, po
+
+
 def merge_partials(part_m: torch.Tensor, part_l: torch.Tensor, part_o: torch.Tensor,
                    out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Merge ``[B, Hq, S]`` / ``[B, Hq, S, d]`` fp32 partials into ``[B, Hq, d]`` of ``out_dtype``."""
@@ -218,4 +252,13 @@ def decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, 
     """Single-query decode over a paged cache: paged split-K partials then their merge."""
     pm, pl, po = decode_splitk_paged(q, k_pages, v_pages, block_table, kv_lens, num_splits, scale, partials,
                                      window, alibi_slopes)
+    return merge_partials(pm, pl, po, q.dtype)
+
+
+def decode_q4(q: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Tensor, v_codes: torch.Tensor,
+              v_scales: torch.Tensor, kv_lens: torch.Tensor, rotated: bool, num_splits: Optional[int] = None,
+              scale: Optional[float] = None, partials=None) -> torch.Tensor:
+    """Single-query decode over a 4-bit cache: fused-dequant split-K partials then their merge."""
+    pm, pl, po = decode_splitk_q4(q, k_codes, k_scales, v_codes, v_scales, kv_lens, rotated, num_splits, scale,
+                                  partials)
     return merge_partials(pm, pl, po, q.dtype)

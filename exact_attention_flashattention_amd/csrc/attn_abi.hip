@@ -163,6 +163,29 @@ attn_status attn_decode_splitk_paged(const void* q, const void* k_pages, const v
                                                    static_cast<hipStream_t>(stream)));
 }
 
+attn_status attn_decode_splitk_q4(const void* q, const void* k_codes, const float* k_scales, const void* v_codes,
+                                  const float* v_scales, const int* kv_lens, int max_kv_len, int dtype, int batch,
+                                  int hq, int hkv, int d, float scale, int rotated, int num_splits, float* part_m,
+                                  float* part_l, float* part_o, void* stream) {
+  if (!q || !k_codes || !k_scales || !v_codes || !v_scales || !kv_lens || !part_m || !part_l || !part_o)
+    return ATTN_ERR_NULL_PTR;
+  if (batch < 1 || hq < 1 || hkv < 1 || max_kv_len < 1 || num_splits < 1 || hq % hkv != 0 || !scale_ok(scale))
+    return ATTN_ERR_BAD_SHAPE;
+  if ((d != 64 && d != 128) || !dtype_ok(dtype)) return ATTN_ERR_UNSUPPORTED;
+  const int groups = (hq / hkv + 15) / 16;
+  if ((long long)batch * hkv * max_kv_len * d >= kMaxElems || (long long)max_kv_len * d >= (1LL << 31) ||
+      batch > 65535 || (long long)hkv * groups > 65535 || num_splits > 65535 ||
+      (long long)batch * hq * num_splits * d >= kMaxElems)
+    return ATTN_ERR_TOO_LARGE;
+  if (!aligned16(q) || !aligned16(k_codes) || !aligned16(v_codes) || !aligned16(k_scales) || !aligned16(v_scales) ||
+      !aligned16(part_o))
+    return ATTN_ERR_MISALIGNED;
+  const int chunk = attn_decode_chunk_len(max_kv_len, num_splits);
+  return from_hip(attn::launch_decode_splitk_q4(q, k_codes, k_scales, v_codes, v_scales, kv_lens, max_kv_len,
+                                                dtype == ATTN_BF16, batch, hq, hkv, d, scale, rotated != 0, num_splits,
+                                                chunk, part_m, part_l, part_o, static_cast<hipStream_t>(stream)));
+}
+
 attn_status attn_merge_partials(const float* part_m, const float* part_l, const float* part_o, int batch, int hq,
                                 int d, int num_splits, void* o, int out_dtype, void* stream) {
   if (!part_m || !part_l || !part_o || !o) return ATTN_ERR_NULL_PTR;

@@ -31,6 +31,13 @@ hipError_t launch_decode_splitk_paged(const void* q, const void* k_pages, const 
                                       int num_splits, int chunk, int window, const float* alibi, float* part_m,
                                       float* part_l, float* part_o, hipStream_t stream);
 
+// 4-bit (E2M1 codes + fp32 row scales) caches [B, hkv, max_kv_len, d/2] and
+// [B, hkv, max_kv_len]; `rotated`: rows stored in the normalised Hadamard domain.
+hipError_t launch_decode_splitk_q4(const void* q, const void* k_codes, const float* k_scales, const void* v_codes,
+                                   const float* v_scales, const int* kv_lens, int max_kv_len, bool bf16, int batch,
+                                   int hq, int hkv, int d, float scale, bool rotated, int num_splits, int chunk,
+                                   float* part_m, float* part_l, float* part_o, hipStream_t stream);
+
 hipError_t launch_merge(const float* part_m, const float* part_l, const float* part_o, int rows, int d,
                         int num_splits, bool bf16, void* out, hipStream_t stream);
 

@@ -220,6 +220,38 @@ attn_status attn_decode_splitk_paged(const void* q, const void* k_pages, const v
                                      float* part_l, float* part_o, void* stream);
 
 /*
+ * attn_decode_splitk_q4 -- attn_decode_splitk over a 4-bit KV cache,
+ * dequantised inside the tile loads: the kernel reads only the codes and the
+ * row scales ("Why a quantised cache needs a fused kernel" on "Attention from
+ * the kernel's side": a separate dequantise pass would move more bytes than
+ * the 16-bit cache it replaces).
+ *
+ *   q        : [batch, hq, d]                     elements of `dtype`
+ *   k_codes  : [batch, hkv, max_kv_len, d/2] bytes; byte i of a row holds
+ *              elements 2i (low nibble) and 2i+1 (high nibble), each an OCP
+ *              MX E2M1 code (bit 3 sign, bits 2:1 exponent with bias 1, bit 0
+ *              mantissa: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6)
+ *   k_scales : [batch, hkv, max_kv_len] fp32; row value = code value × scale
+ *   v_codes, v_scales : the same for V
+ *   rotated  : 0 = rows hold k and v; 1 = rows hold R·k and R·v with
+ *              R = H_d / sqrt(d), the normalised Sylvester-Hadamard matrix
+ *              (H_1 = [1], H_2n = [[H_n, H_n], [H_n, -H_n]]).  The kernel
+ *              rotates q by R on load and the partial outputs back by R (R is
+ *              its own inverse), so q and the outputs are always unrotated.
+ *   kv_lens, max_kv_len, num_splits, part_m, part_l, part_o : as for
+ *              attn_decode_splitk; the partials are merged by
+ *              attn_merge_partials.
+ *
+ * The result is attention over the dequantised cache (code value × scale,
+ * rotated back when `rotated`), computed with the same split-K recurrence.
+ * Every pointer must be 16-byte aligned.  Limits as for attn_decode_splitk.
+ */
+attn_status attn_decode_splitk_q4(const void* q, const void* k_codes, const float* k_scales, const void* v_codes,
+                                  const float* v_scales, const int* kv_lens, int max_kv_len, int dtype, int batch,
+                                  int hq, int hkv, int d, float scale, int rotated, int num_splits, float* part_m,
+                                  float* part_l, float* part_o, void* stream);
+
+/*
  * attn_merge_partials -- merge the partial states of each (sequence, head)
  * and normalise: m = max_s m_s, l = sum_s l_s·exp(m_s − m),
  * o = sum_s o_s·exp(m_s − m), O = o / l (the two-state merge rule of "Maths"

@@ -17,6 +17,10 @@ from .attention import (  # noqa: F401
     attention_varlen,
     decode,
     decode_paged,
+    decode_q4,
+    dequantize_e2m1_rows,
+    e2m1_value,
+    hadamard,
     gather_pages,
     merge_pair,
     merge_partials,

@@ -268,6 +268,60 @@ def decode_paged(q, k_pages, v_pages, block_table, kv_lens, scale: float, window
     return out
 
 
+def e2m1_value(code):
+    """Value of 4-bit OCP MX E2M1 codes: bit 3 sign, bits 2:1 exponent e
+    (bias 1), bit 0 mantissa m; e = 0 is subnormal, 0.5·m; otherwise
+    2^(e-1)·(1 + m/2)."""
+    c = np.asarray(code, dtype=np.int64)
+    sign = (c >> 3) & 1
+    e = (c >> 1) & 3
+    m = c & 1
+    mag = np.where(e == 0, 0.5 * m, np.exp2(e - 1.0) * (1.0 + 0.5 * m))
+    return np.where(sign == 1, -mag, mag)
+
+
+def hadamard(d: int):
+    """Normalised Sylvester-Hadamard matrix H_d / sqrt(d): H_1 = [1],
+    H_2n = [[H_n, H_n], [H_n, -H_n]].  Orthogonal and symmetric."""
+    h = np.ones((1, 1))
+    while h.shape[0] < d:
+        h = np.block([[h, h], [h, -h]])
+    if h.shape[0] != d:
+        raise ValueError(f"d={d} is not a power of two")
+    return h / math.sqrt(d)
+
+
+def dequantize_e2m1_rows(codes, scales, rotated: bool):
+    """Rows ``[..., d]`` of a 4-bit cache: byte i of a row gives element 2i
+    (low nibble) and 2i+1 (high nibble), each code's value times the row's
+    scale; with ``rotated`` the stored row is R·x (R = ``hadamard(d)``), so x
+    is R times it."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    lo, hi = codes & 15, codes >> 4
+    vals = np.stack([e2m1_value(lo), e2m1_value(hi)], axis=-1).reshape(codes.shape[:-1] + (2 * codes.shape[-1],))
+    vals = vals * _f64(scales)[..., None]
+    if rotated:
+        vals = vals @ hadamard(vals.shape[-1])
+    return vals
+
+
+def decode_q4(q, k_codes, k_scales, v_codes, v_scales, kv_lens, scale: float, rotated: bool):
+    """Single-query attention over a 4-bit cache: the rows are dequantised and
+    the plain ``decode`` runs on them ("Why a quantised cache needs a fused
+    kernel" on "Attention from the kernel's side": fusing the dequantisation
+    changes the bytes read, not the result).  Only rows below each length are
+    dequantised."""
+    B, Hkv, L = np.asarray(k_scales).shape
+    d = 2 * np.asarray(k_codes).shape[-1]
+    K = np.zeros((B, Hkv, L, d))
+    V = np.zeros((B, Hkv, L, d))
+    for b in range(B):
+        n = int(kv_lens[b])
+        K[b, :, :n] = dequantize_e2m1_rows(np.asarray(k_codes)[b, :, :n], np.asarray(k_scales)[b, :, :n], rotated)
+        V[b, :, :n] = dequantize_e2m1_rows(np.asarray(v_codes)[b, :, :n], np.asarray(v_scales)[b, :, :n], rotated)
+    return decode(q, K, V, kv_lens, scale)
+
+
 def _merge_arrays(ma, la, oa, mb, lb, ob):
     """The two-state merge rule, elementwise over any leading shape.
 

@@ -110,6 +110,24 @@ def test_decode_paged_rejects_bad_arguments(lib, kw, status):
     assert decode_paged(lib, **kw) == status
 
 
+def decode_q4(lib, q=P, kc=P, ks=P, vc=P, vs=P, lens=P, L=100, dtype=BF16, batch=1, hq=4, hkv=2, d=128, scale=0.1,
+              rot=1, S=2, pm=P, pl=P, po=P):
+    return lib.attn_decode_splitk_q4(q, kc, ks, vc, vs, lens, L, dtype, batch, hq, hkv, d, scale, rot, S, pm, pl, po,
+                                     None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), NULL), (dict(kc=None), NULL), (dict(ks=None), NULL), (dict(vc=None), NULL), (dict(vs=None), NULL),
+    (dict(lens=None), NULL), (dict(po=None), NULL),
+    (dict(L=0), SHAPE), (dict(S=0), SHAPE), (dict(hq=3), SHAPE), (dict(scale=0.0), SHAPE),
+    (dict(d=96), UNSUP), (dict(dtype=9), UNSUP),
+    (dict(kc=P + 4), MISAL), (dict(ks=P + 4), MISAL), (dict(vs=P + 8), MISAL),
+    (dict(batch=70000), BIG), (dict(L=1 << 25), BIG),
+])
+def test_decode_q4_rejects_bad_arguments(lib, kw, status):
+    assert decode_q4(lib, **kw) == status
+
+
 @pytest.mark.parametrize("args,status", [
     ((None, P, P, 1, 2, 64, 3, P, BF16), NULL), ((P, P, P, 0, 2, 64, 3, P, BF16), SHAPE),
     ((P, P, P, 1, 2, 64, 0, P, BF16), SHAPE), ((P, P, P, 1, 2, 72, 3, P, BF16), UNSUP),

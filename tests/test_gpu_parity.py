@@ -525,6 +525,60 @@ def test_decode_paged_long_context_full(A):
     assert_close(out, ref, f"paged {DEC.name}")
 
 
+# --- 4-bit cache, fused dequant ---------------------------------------------------------
+
+def q4_case(A, w, kv_lens, max_len, batch, num_splits, rotated, seed=0):
+    announce(f"q4 {w.name} B={batch} L={max_len} lens={kv_lens.tolist()[:6]} S={num_splits} rotated={rotated}")
+    q, kq, ks, vq, vs, lens = workloads.decode_q4_inputs(w, rotated, device=DEV, salt=seed, kv_lens=kv_lens,
+                                                         max_kv_len=max_len, batch=batch)
+    S = A.decode_num_splits(batch, w.hkv, max_len) if num_splits is None else num_splits
+    out = A.decode_q4(q, kq, ks, vq, vs, lens.to(DEV), rotated, S, w.scale)
+    torch.cuda.synchronize()
+    ref = oracle.decode_q4(f64(q), kq.cpu().numpy(), ks.cpu().double().numpy(), vq.cpu().numpy(),
+                           vs.cpu().double().numpy(), lens.numpy(), w.scale, rotated)
+    assert_close(out, ref, f"q4 {w.name} S={S} rotated={rotated}")
+    return out
+
+
+@pytest.mark.parametrize("rotated", [False, True])
+@pytest.mark.parametrize("S", [1, None, 7])
+def test_decode_q4_lengths_and_splits(A, S, rotated):
+    """Lengths 1, 2, around the split size and the full cache; NaN scales and
+    arbitrary codes past each length are never used."""
+    lens = torch.tensor([1, 2, 63, 64, 65, 700, 1024], dtype=torch.int32)
+    q4_case(A, DEC, lens, 1024, len(lens), S, rotated)
+
+
+@pytest.mark.parametrize("hq,hkv,d,dtype", [(4, 4, 128, "bf16"), (16, 1, 64, "bf16"), (24, 1, 128, "f16"),
+                                            (32, 2, 64, "f16"), (8, 8, 64, "bf16")])
+@pytest.mark.parametrize("rotated", [False, True])
+def test_decode_q4_head_layouts(A, hq, hkv, d, dtype, rotated):
+    w = workloads.Decode(f"decode_q4_case_{hq}_{hkv}_{d}_{dtype}", 3, hq, hkv, d, 700, None, 1.0, dtype)
+    q4_case(A, w, torch.tensor([700, 333, 64], dtype=torch.int32), 700, 3, None, rotated)
+
+
+def test_decode_q4_ragged_high_scores(A):
+    """The ragged workload's recipe (q x8, scores far past fp16's exp range), reduced."""
+    q4_case(A, RAG, torch.tensor([1024, 3000, 1500, 4096], dtype=torch.int32), 4096, 4, None, True)
+
+
+def test_decode_q4_long_context_full(A):
+    """The 262144-key cache encoded as rotated 4-bit rows, the benchmarked launch,
+    whole output against the oracle on the dequantised rows."""
+    announce(f"q4 {DEC.name}")
+    q, kq, ks, vq, vs, lens = workloads.decode_q4_inputs(DEC, True, device=DEV)
+    out = A.decode_q4(q, kq, ks, vq, vs, lens.to(DEV), True, None, DEC.scale)
+    torch.cuda.synchronize()
+    g = DEC.hq // DEC.hkv
+    qf = f64(q)
+    ref = np.zeros((1, DEC.hq, DEC.d))
+    for kh in range(DEC.hkv):
+        K = oracle.dequantize_e2m1_rows(kq[0, kh].cpu().numpy(), ks[0, kh].cpu().double().numpy(), True)
+        V = oracle.dequantize_e2m1_rows(vq[0, kh].cpu().numpy(), vs[0, kh].cpu().double().numpy(), True)
+        ref[0, kh * g:(kh + 1) * g] = oracle.attention_rows(qf[0, kh * g:(kh + 1) * g], K, V, DEC.scale)
+    assert_close(out, ref, f"q4 {DEC.name}")
+
+
 # --- merge -----------------------------------------------------------------------------
 
 @pytest.mark.parametrize("S", [1, 2, 9, 300])

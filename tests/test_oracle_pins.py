@@ -566,6 +566,70 @@ def test_paged_decode_masks_equal_last_row_of_varlen(window, alibi):
         assert np.max(np.abs(got - oracle.decode_paged(q, kp, vp, table, lens, 0.3, 0, slopes))) > 1e-3
 
 
+# --- 4-bit cache (E2M1 codes, row scales, optional Hadamard rotation) ---
+
+def test_e2m1_code_values():
+    """All 16 codes, written out from the format's bit fields by hand."""
+    want = [0, 0.5, 1, 1.5, 2, 3, 4, 6, -0.0, -0.5, -1, -1.5, -2, -3, -4, -6]
+    got = oracle.e2m1_value(np.arange(16))
+    assert np.array_equal(got, np.array(want, dtype=float))
+    assert np.signbit(got[8]) and not np.signbit(got[0])
+
+
+@pytest.mark.parametrize("d", [1, 2, 4, 8, 16, 64, 128])
+def test_hadamard_is_scipy_hadamard_normalised_and_its_own_inverse(d):
+    import scipy.linalg
+    R = oracle.hadamard(d)
+    assert np.array_equal(R * math.sqrt(d), scipy.linalg.hadamard(d).astype(float))
+    assert np.max(np.abs(R @ R - np.eye(d))) <= 1e-14 and np.array_equal(R, R.T)
+
+
+def test_dequantize_nibble_order_and_scale():
+    """Bytes 0x21, 0xF1, 0xA5 hold (low, high) nibbles (1, 2), (1, 15), (5, 10):
+    values (0.5, 1), (0.5, -6), (3, -1), times the row scale 0.75."""
+    got = oracle.dequantize_e2m1_rows(np.array([[0x21, 0xF1, 0xA5]], dtype=np.uint8), np.array([0.75]), False)
+    assert np.array_equal(got, 0.75 * np.array([[0.5, 1, 0.5, -6, 3, -1]]))
+    rot = oracle.dequantize_e2m1_rows(np.array([[0x21, 0xF1]], dtype=np.uint8), np.array([2.0]), True)
+    plain = 2.0 * np.array([0.5, 1, 0.5, -6])
+    H = np.array([[1, 1, 1, 1], [1, -1, 1, -1], [1, 1, -1, -1], [1, -1, -1, 1]]) / 2.0
+    assert np.max(np.abs(rot[0] - H @ plain)) <= 1e-15
+
+
+@pytest.mark.parametrize("rotated", [False, True])
+def test_encoder_decoder_round_trip_within_half_a_step(rotated):
+    """The input encoder and the oracle's decoder agree: each element lands on
+    the nearest E2M1 magnitude, so the error in the stored domain is at most
+    half the gap around it times the scale (the largest half gap is 1, between
+    4 and 6); the rotation preserves the error's norm."""
+    x = torch.randn(64, 128, generator=torch.Generator().manual_seed(3), dtype=torch.float32)
+    codes, scales = workloads.quantize_e2m1_rows(x, rotated)
+    back = oracle.dequantize_e2m1_rows(codes.numpy(), scales.numpy(), rotated)
+    xs = x.double().numpy() @ (oracle.hadamard(128) if rotated else np.eye(128))
+    bs = back @ (oracle.hadamard(128) if rotated else np.eye(128))
+    t = np.abs(xs) / scales.double().numpy()[:, None]
+    half_gap = np.select([t <= 2, t <= 4], [0.25, 0.5], 1.0)
+    assert np.all(np.abs(bs - xs) <= half_gap * scales.double().numpy()[:, None] * (1 + 1e-6))
+    assert np.allclose(np.linalg.norm(back - x.double().numpy(), axis=1), np.linalg.norm(bs - xs, axis=1))
+    assert np.all(np.abs(t).max(axis=1) <= 6 * (1 + 1e-6))
+
+
+def test_decode_q4_is_decode_on_dequantised_rows_and_single_key_exact():
+    B, hq, hkv, L, d = 2, 4, 2, 40, 16
+    rng = np.random.default_rng(140)
+    kc = rng.integers(0, 256, (B, hkv, L, d // 2), dtype=np.uint8)
+    vc = rng.integers(0, 256, (B, hkv, L, d // 2), dtype=np.uint8)
+    ks, vs = rng.uniform(0.1, 1, (B, hkv, L)), rng.uniform(0.1, 1, (B, hkv, L))
+    q = gauss(141, B, hq, d)
+    for rotated in (False, True):
+        got = oracle.decode_q4(q, kc, ks, vc, vs, [40, 1], 0.25, rotated)
+        K = oracle.dequantize_e2m1_rows(kc, ks, rotated)
+        V = oracle.dequantize_e2m1_rows(vc, vs, rotated)
+        assert np.max(np.abs(got - oracle.decode(q, K, V, [40, 1], 0.25))) <= TOL
+        # one key: its V row (exactly when unrotated; the rotated row through a different matmul shape)
+        single = np.repeat(V[1, :, 0], hq // hkv, axis=0)
+        assert np.array_equal(got[1], single) if not rotated else np.max(np.abs(got[1] - single)) <= TOL
+
+
 def test_attention_rows_matches_full_output():
     B, hq, n, d = 1, 2, 130, 32
     q, k, v = gauss(62, B, hq, n, d), gauss(63, B, hq, n, d), gauss(64, B, hq, n, d)
