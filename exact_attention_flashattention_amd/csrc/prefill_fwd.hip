@@ -194,18 +194,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // Variable-length batches: (sequence, KV head) units are dealt round-robin
   // to the XCDs instead, so that with hkv a multiple of 8 every XCD holds the
   // same KV heads of every sequence -- unequal sequences then load all XCDs
-  // alike -- and the query heads sharing a KV head stay on one XCD; each XCD
-  // walks its units' query tiles from the last tile down.
+  // alike -- and the query heads sharing a KV head stay on one XCD.  An XCD
+  // takes its units one after another, each unit's query tiles from the last
+  // down with the unit's query heads side by side, so the tiles that stream
+  // the same K and V run close together and share them in the XCD's L2.
   int b, h, qt;
   if constexpr (VARLEN) {
     const int g = hq / hkv;
     const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
-    const int per = (batch * hkv - xcd + 7) / 8 * g;  // work items of this XCD per query-tile index
-    if (slot >= per * num_q_tiles) return;            // (the whole workgroup)
-    qt = num_q_tiles - 1 - slot / per;
-    const int unit = xcd + 8 * ((slot % per) / g);
+    const int units = (batch * hkv - xcd + 7) / 8;   // units of this XCD
+    const int per_unit = g * num_q_tiles;            // work items of one unit
+    if (slot >= units * per_unit) return;            // (the whole workgroup)
+    const int unit = xcd + 8 * (slot / per_unit);
+    qt = num_q_tiles - 1 - (slot % per_unit) / g;
     b = unit / hkv;
-    h = (unit % hkv) * g + (slot % per) % g;
+    h = (unit % hkv) * g + (slot % per_unit) % g;
   } else {
     const int H = batch * hq;
     int bh;
