@@ -15,6 +15,7 @@ Entry points (same names as the C ABI):
   ``attn_decode_splitk_paged``
 * ``decode_splitk_q4(q, k_codes, k_scales, v_codes, v_scales, kv_lens, rotated, num_splits, scale)`` --
   ``attn_decode_splitk_q4``
+* ``kv_quantize_q4(x, rotated, out_rows, codes, scales)`` -- ``attn_kv_quantize_q4``
 * ``merge_partials(part_m, part_l, part_o, out_dtype)`` -- ``attn_merge_partials``
 * ``decode(...)``, ``decode_paged(...)``, ``decode_q4(...)`` -- split-K then merge, back to back on one stream
 * ``decode_num_splits``, ``decode_chunk_len``, ``decode_workspace_bytes`` -- host helpers
@@ -30,7 +31,7 @@ import torch
 from . import _lib
 from ._lib import ATTN_BF16, ATTN_F16, AttnError  # noqa: F401
 
-__all__ = ["prefill_fwd", "prefill_varlen_fwd", "decode_splitk", "decode_splitk_paged", "decode_splitk_q4", "decode_q4", "merge_partials", "decode", "decode_paged",
+__all__ = ["prefill_fwd", "prefill_varlen_fwd", "decode_splitk", "decode_splitk_paged", "decode_splitk_q4", "decode_q4", "kv_quantize_q4", "merge_partials", "decode", "decode_paged",
            "decode_num_splits", "decode_chunk_len", "decode_workspace_bytes", "AttnError"]
 
 _DTYPES = {torch.bfloat16: ATTN_BF16, torch.float16: ATTN_F16}
@@ -220,6 +221,34 @@ def decode_splitk_q4(q: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Ten
                                    _dev(pm, "part_m"), _dev(pl, "part_l"), _dev(po, "part_o"), _stream(q))
     _lib.check("attn_decode_splitk_q4", st)
     return pm, pl, po
+
+
+def kv_quantize_q4(x: torch.Tensor, rotated: bool, out_rows: Optional[torch.Tensor] = None,
+                   codes: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None):
+    """Encode rows ``x [..., d]`` (bf16/fp16, device) into 4-bit cache rows: returns ``(codes, scales)``,
+    ``codes [..., d/2]`` uint8 and ``scales [...]`` fp32.  With ``out_rows`` (int32 device ``[rows]``) row i is
+    written to row ``out_rows[i]`` of the given flat ``codes [capacity, d/2]`` / ``scales [capacity]``."""
+    lib = _lib_handle()
+    d = x.shape[-1]
+    rows = x.numel() // d
+    if out_rows is None:
+        if codes is None:
+            codes = torch.empty(x.shape[:-1] + (d // 2,), dtype=torch.uint8, device=x.device)
+            scales = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+        capacity = rows
+    else:
+        if codes is None or scales is None:
+            raise ValueError("out_rows needs the destination codes and scales")
+        if out_rows.dtype != torch.int32 or out_rows.numel() != rows or out_rows.device != x.device:
+            raise ValueError("out_rows must be an int32 device tensor with one entry per row")
+        capacity = scales.numel()
+    if codes.dtype != torch.uint8 or scales.dtype != torch.float32 or codes.numel() != scales.numel() * (d // 2):
+        raise ValueError("codes must be uint8 [capacity, d/2] and scales float32 [capacity]")
+    st = lib.attn_kv_quantize_q4(_dev(x, "x"), rows, d, _dtype_code(x), int(bool(rotated)),
+                                 None if out_rows is None else _dev(out_rows, "out_rows"), capacity,
+                                 _dev(codes, "codes"), _dev(scales, "scales"), _stream(x))
+    _lib.check("attn_kv_quantize_q4", st)
+    return codes, scales
 
 
 def merge_partials(part_m: torch.Tensor, part_l: torch.Tensor, part_o: torch.Tensor,

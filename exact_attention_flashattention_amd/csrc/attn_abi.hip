@@ -186,6 +186,18 @@ attn_status attn_decode_splitk_q4(const void* q, const void* k_codes, const floa
                                                 chunk, part_m, part_l, part_o, static_cast<hipStream_t>(stream)));
 }
 
+attn_status attn_kv_quantize_q4(const void* x, int rows, int d, int dtype, int rotated, const int* out_rows,
+                                int out_capacity, void* codes, float* scales, void* stream) {
+  if (!x || !codes || !scales) return ATTN_ERR_NULL_PTR;
+  if (rows < 1 || out_capacity < 1 || (!out_rows && rows > out_capacity)) return ATTN_ERR_BAD_SHAPE;
+  if ((d != 64 && d != 128) || !dtype_ok(dtype)) return ATTN_ERR_UNSUPPORTED;
+  if ((long long)rows * d >= kMaxElems || (long long)out_capacity * d >= kMaxElems) return ATTN_ERR_TOO_LARGE;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return ATTN_ERR_MISALIGNED;
+  const float norm = (float)(1.0 / std::sqrt((double)d));
+  return from_hip(attn::launch_quantize_q4(x, rows, d, dtype == ATTN_BF16, rotated != 0, norm, out_rows, out_capacity,
+                                           codes, scales, static_cast<hipStream_t>(stream)));
+}
+
 attn_status attn_merge_partials(const float* part_m, const float* part_l, const float* part_o, int batch, int hq,
                                 int d, int num_splits, void* o, int out_dtype, void* stream) {
   if (!part_m || !part_l || !part_o || !o) return ATTN_ERR_NULL_PTR;

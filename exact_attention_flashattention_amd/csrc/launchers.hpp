@@ -38,6 +38,11 @@ hipError_t launch_decode_splitk_q4(const void* q, const void* k_codes, const flo
                                    int hq, int hkv, int d, float scale, bool rotated, int num_splits, int chunk,
                                    float* part_m, float* part_l, float* part_o, hipStream_t stream);
 
+// Rows [rows, d] of 16-bit values -> E2M1 codes [.., d/2] and fp32 scales, row i
+// written to row out_rows[i] (or i) of the outputs when inside [0, out_capacity).
+hipError_t launch_quantize_q4(const void* x, int rows, int d, bool bf16, bool rotated, float norm, const int* out_rows,
+                              int out_capacity, void* codes, float* scales, hipStream_t stream);
+
 hipError_t launch_merge(const float* part_m, const float* part_l, const float* part_o, int rows, int d,
                         int num_splits, bool bf16, void* out, hipStream_t stream);
 

@@ -252,6 +252,32 @@ attn_status attn_decode_splitk_q4(const void* q, const void* k_codes, const floa
                                   float* part_l, float* part_o, void* stream);
 
 /*
+ * attn_kv_quantize_q4 -- encode rows of keys or values into the 4-bit cache
+ * format read by attn_decode_splitk_q4 (the write side of the fused-dequant
+ * cache: rows are quantised once, as they enter the cache).
+ *
+ *   x        : [rows, d] elements of `dtype`, DEVICE memory, read
+ *   rotated  : 0 = encode x; 1 = encode R·x (R = H_d / sqrt(d) as above)
+ *   out_rows : NULL (row i goes to output row i; then rows <= out_capacity)
+ *              or [rows] int32 DEVICE memory: row i goes to output row
+ *              out_rows[i]; a destination outside [0, out_capacity) is
+ *              skipped (nothing written).  E.g. appending one position to a
+ *              [batch, hkv, max_kv_len] cache: (b·hkv + kh)·max_kv_len + pos.
+ *   codes    : [out_capacity, d/2] bytes, written (E2M1 pairs as above)
+ *   scales   : [out_capacity] fp32, written
+ *
+ * Per row, in fp32 and in this order: with `rotated` the Walsh-Hadamard
+ * butterflies over the element index bits from bit 0 upward (lower element
+ * a, upper b -> a + b, a - b) and one multiplication by 1/sqrt(d) rounded to
+ * fp32; scale = max|y| / 6 (1 for an all-zero row); each element's code is the
+ * nearest E2M1 magnitude of |y / scale| (ties to the even code) with the sign
+ * bit set when y / scale < 0.  Inputs must be finite.  x, codes and scales
+ * must be 16-byte aligned.
+ */
+attn_status attn_kv_quantize_q4(const void* x, int rows, int d, int dtype, int rotated, const int* out_rows,
+                                int out_capacity, void* codes, float* scales, void* stream);
+
+/*
  * attn_merge_partials -- merge the partial states of each (sequence, head)
  * and normalise: m = max_s m_s, l = sum_s l_s·exp(m_s − m),
  * o = sum_s o_s·exp(m_s − m), O = o / l (the two-state merge rule of "Maths"

@@ -128,6 +128,20 @@ def test_decode_q4_rejects_bad_arguments(lib, kw, status):
     assert decode_q4(lib, **kw) == status
 
 
+def quant(lib, x=P, rows=10, d=128, dtype=BF16, rot=1, out_rows=None, cap=10, codes=P, scales=P):
+    return lib.attn_kv_quantize_q4(x, rows, d, dtype, rot, out_rows, cap, codes, scales, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), NULL), (dict(codes=None), NULL), (dict(scales=None), NULL),
+    (dict(rows=0), SHAPE), (dict(cap=0), SHAPE), (dict(rows=11), SHAPE),
+    (dict(d=32), UNSUP), (dict(dtype=4), UNSUP),
+    (dict(x=P + 2), MISAL), (dict(codes=P + 8), MISAL), (dict(scales=P + 4), MISAL),
+])
+def test_kv_quantize_rejects_bad_arguments(lib, kw, status):
+    assert quant(lib, **kw) == status
+
+
 @pytest.mark.parametrize("args,status", [
     ((None, P, P, 1, 2, 64, 3, P, BF16), NULL), ((P, P, P, 0, 2, 64, 3, P, BF16), SHAPE),
     ((P, P, P, 1, 2, 64, 0, P, BF16), SHAPE), ((P, P, P, 1, 2, 72, 3, P, BF16), UNSUP),

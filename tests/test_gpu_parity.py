@@ -579,6 +579,65 @@ def test_decode_q4_long_context_full(A):
     assert_close(out, ref, f"q4 {DEC.name}")
 
 
+@pytest.mark.parametrize("d,dtype", [(128, "bf16"), (64, "bf16"), (128, "f16"), (64, "f16")])
+@pytest.mark.parametrize("rotated", [False, True])
+def test_kv_quantize_q4_matches_the_host_encoder_bit_exact(A, d, dtype, rotated):
+    """The HIP encoder and the independent host encoder follow the same fixed
+    fp32 procedure, so codes and scales agree bit for bit; rows include an
+    all-zero row (scale 1) and exact code-boundary values."""
+    announce(f"quantize d={d} {dtype} rotated={rotated}")
+    x = workloads.normal((37, 5, d), dtype, workloads.seed_for("quantize", "x", d), DEV) * 3
+    x[0, 0] = 0
+    x[1, 1, :8] = torch.tensor([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0], dtype=x.dtype)
+    codes, scales = A.kv_quantize_q4(x, rotated)
+    torch.cuda.synchronize()
+    ref_c, ref_s = workloads.quantize_e2m1_rows(x.cpu(), rotated)
+    assert torch.equal(scales.cpu(), ref_s)
+    assert torch.equal(codes.cpu(), ref_c)
+    assert scales[0, 0].item() == 1.0 and not codes[0, 0].any()
+
+
+def test_kv_quantize_q4_scatters_rows_and_skips_outside(A):
+    """Appending one position per (sequence, KV head) to a [B, Hkv, L] cache:
+    rows land at (b·Hkv + kh)·L + pos; a destination outside the cache is
+    skipped and the rest of the cache is untouched."""
+    announce("quantize scatter")
+    B, hkv, L, d = 3, 2, 16, 128
+    x = workloads.normal((B, hkv, d), "bf16", workloads.seed_for("quantize", "scatter"), DEV)
+    pos = torch.tensor([5, 0, 15], dtype=torch.int32)
+    dst = ((torch.arange(B)[:, None] * hkv + torch.arange(hkv)[None, :]) * L + pos[:, None]).to(torch.int32)
+    dst[2, 1] = B * hkv * L + 7  # outside: skipped
+    codes = torch.full((B * hkv * L, d // 2), 0xAB, dtype=torch.uint8, device=DEV)
+    scales = torch.full((B * hkv * L,), -1.0, dtype=torch.float32, device=DEV)
+    A.kv_quantize_q4(x, True, dst.reshape(-1).to(DEV), codes, scales)
+    torch.cuda.synchronize()
+    ref_c, ref_s = workloads.quantize_e2m1_rows(x.cpu().reshape(-1, d), True)
+    written = torch.zeros(B * hkv * L, dtype=torch.bool)
+    for i, r in enumerate(dst.reshape(-1).tolist()):
+        if r < B * hkv * L:
+            assert torch.equal(codes[r].cpu(), ref_c[i]) and scales[r].item() == ref_s[i].item()
+            written[r] = True
+    assert int(written.sum()) == B * hkv - 1
+    assert (codes.cpu()[~written] == 0xAB).all() and (scales.cpu()[~written] == -1.0).all()
+
+
+def test_kv_quantize_then_fused_decode(A):
+    """End to end on the device: a bf16 cache encoded by the HIP encoder and read by
+    the fused-dequant decode equals the oracle on the dequantised rows."""
+    announce("quantize + q4 decode")
+    w = DEC
+    lens = torch.tensor([700, 1024, 33], dtype=torch.int32)
+    q, kc, vc, lens = workloads.decode_inputs(w, device=DEV, kv_lens=lens, max_kv_len=1024, batch=3)
+    kc, vc = torch.nan_to_num(kc), torch.nan_to_num(vc)  # the encoder takes finite rows
+    kq, ks = A.kv_quantize_q4(kc, True)
+    vq, vs = A.kv_quantize_q4(vc, True)
+    out = A.decode_q4(q, kq, ks, vq, vs, lens.to(DEV), True, None, w.scale)
+    torch.cuda.synchronize()
+    ref = oracle.decode_q4(f64(q), kq.cpu().numpy(), ks.cpu().double().numpy(), vq.cpu().numpy(),
+                           vs.cpu().double().numpy(), lens.numpy(), w.scale, True)
+    assert_close(out, ref, "quantize + q4 decode")
+
+
 # --- merge -----------------------------------------------------------------------------
 
 @pytest.mark.parametrize("S", [1, 2, 9, 300])

@@ -281,19 +281,12 @@ def paged_from_cache(k_cache: torch.Tensor, v_cache: torch.Tensor, kv_lens: torc
 _E2M1_MAGNITUDES = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
 
 
-def _sylvester(d: int) -> torch.Tensor:
-    h = torch.ones(1, 1, dtype=torch.float64)
-    while h.shape[0] < d:
-        h = torch.cat([torch.cat([h, h], 1), torch.cat([h, -h], 1)], 0)
-    if h.shape[0] != d:
-        raise ValueError(f"d={d} is not a power of two")
-    return h / math.sqrt(d)
-
-
 def quantize_e2m1_rows(x: torch.Tensor, rotated: bool):
     """Encode rows ``x [..., d]`` as ``(codes uint8 [..., d/2], scales float32 [...])``.
 
-    The row (rotated by R first if ``rotated``) is divided by its scale
+    The row (rotated by R first if ``rotated``: fp32 butterflies over the
+    index bits from bit 0 upward, then a multiplication by fp32(1/sqrt(d))) is
+    divided by its scale
     ``max|row| / 6`` (1 for an all-zero row) and every element takes the code
     of the nearest E2M1 magnitude (ties to the even code), with the sign bit
     set for negative values.  Rows holding NaN keep a NaN scale.
@@ -301,7 +294,15 @@ def quantize_e2m1_rows(x: torch.Tensor, rotated: bool):
     d = x.shape[-1]
     y = x.float()
     if rotated:
-        y = y @ _sylvester(d).to(device=x.device, dtype=torch.float32)
+        # R·x as fp32 butterflies over the index bits from bit 0 upward, then one
+        # multiplication by 1/sqrt(d) rounded to fp32 (a fixed procedure, so that
+        # every encoder following it produces the same codes)
+        h = 1
+        while h < d:
+            v = y.reshape(*y.shape[:-1], d // (2 * h), 2, h)
+            y = torch.stack([v[..., 0, :] + v[..., 1, :], v[..., 0, :] - v[..., 1, :]], dim=-2).reshape(y.shape)
+            h *= 2
+        y = y * torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32)
     amax = y.abs().amax(dim=-1)
     scale = torch.where(amax > 0, amax / 6.0, torch.ones_like(amax))
     scale = torch.where(torch.isnan(amax), amax, scale).to(torch.float32)
