@@ -65,6 +65,7 @@ KERNEL_SOURCES = {
     "decode_splitk_kernel": ["decode_splitk.hip", "device_common.hpp"],
     "merge_partials_kernel": ["merge_partials.hip", "device_common.hpp"],
     "decode_q4_kernel": ["decode_q4.hip", "device_common.hpp"],
+    "quantize_q4_kernel": ["quantize_q4.hip", "device_common.hpp"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
