@@ -132,10 +132,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const int lane = threadIdx.x;
   const int r = lane & 15;
   const int grp = lane >> 4;
-  const int split = blockIdx.x;
   const int kh = blockIdx.y % hkv;
   const int qgrp = blockIdx.y / hkv;
   const int b = blockIdx.z;
+  // split index rotated by the head's number, as in decode_splitk.hip (spreads the
+  // waves that run together over different offsets of their heads' cache regions)
+  const int split = (int)((blockIdx.x + (unsigned)(b * hkv + kh) * 5u) % (unsigned)num_splits);
   const int qi = qgrp * 16 + r;
   const bool qvalid = qi < g;
   const int h = kh * g + (qvalid ? qi : 0);

@@ -91,10 +91,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   const int lane = threadIdx.x;
   const int r = lane & 15;                // MFMA column: query within the group / row within a tile
   const int grp = lane >> 4;              // lane group 0..3
-  const int split = blockIdx.x;
   const int kh = blockIdx.y % hkv;
   const int qgrp = blockIdx.y / hkv;
   const int b = blockIdx.z;
+  // Blocks of one (sequence, KV head) are dispatched together; rotating their
+  // split index by the head's number puts the waves that run at the same time
+  // at different offsets of their heads' cache regions.  With power-of-two
+  // region sizes and ragged lengths, unrotated waves of many heads read the
+  // same offsets at once and contend for the same DRAM banks (measured on 64
+  // ragged sequences in a 32768-position cache: 4.4 -> 5.35 TB/s).
+  const int split = (int)((blockIdx.x + (unsigned)(b * hkv + kh) * 5u) % (unsigned)num_splits);
   const int qi = qgrp * 16 + r;           // query index within the KV head's group
   const bool qvalid = qi < g;
   const int h = kh * g + (qvalid ? qi : 0);
