@@ -15,7 +15,9 @@
 // its own maximum in registers, then the groups are merged through LDS with
 // the same rule -- one round trip to memory.  A workgroup covers COLS output
 // columns: all D when there are many rows, 32 when few rows would leave most
-// of the GPU idle.  Memory-bound: it reads S·(D+2) floats per row once.
+// of the GPU idle.  Reads S·(D+2) floats per row once; with few rows it is
+// bound by memory latency, so each split group folds its splits with a
+// running maximum, which keeps all of a thread's loads independent.
 #include "device_common.hpp"
 #include "launchers.hpp"
 
@@ -41,19 +43,26 @@ __global__ __launch_bounds__(256) void merge_partials_kernel(const float* __rest
   const float* l_ = part_l + row * num_splits;
   const float* o_ = part_o + row * (size_t)num_splits * D + col;
 
-  // 1. this group's splits against the group's own maximum
+  // 1. this group's splits, folded one by one against a running maximum mg (the
+  // loads of a split do not wait for the previous split's arithmetic, so a
+  // thread has several splits' loads in flight at once)
   float mg = kNegInf;
-  for (int s = g; s < num_splits; s += GROUPS) mg = fmaxf(mg, m_[s]);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float lsum = 0.f;
-  if (mg != kNegInf) {
 #pragma unroll 4
-    for (int s = g; s < num_splits; s += GROUPS) {
-      const float ms = m_[s];
-      const float w = (ms == kNegInf) ? 0.f : fast_exp2((ms - mg) * kLog2e);
-      acc += w * *reinterpret_cast<const f32x4*>(o_ + (size_t)s * D);
-      lsum += w * l_[s];
+  for (int s = g; s < num_splits; s += GROUPS) {
+    const float ms = m_[s];
+    const float ls = l_[s];
+    const f32x4 os = *reinterpret_cast<const f32x4*>(o_ + (size_t)s * D);
+    if (ms > mg) {  // a new maximum: rescale what is held (nothing yet while mg = -inf)
+      const float a = (mg == kNegInf) ? 0.f : fast_exp2((mg - ms) * kLog2e);
+      acc *= a;
+      lsum *= a;
+      mg = ms;
     }
+    const float w = (ms == kNegInf) ? 0.f : fast_exp2((ms - mg) * kLog2e);
+    acc += w * os;
+    lsum += w * ls;
   }
   acc_s[g][c] = acc;
   if (c == 0) {
