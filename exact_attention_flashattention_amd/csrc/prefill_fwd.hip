@@ -11,12 +11,14 @@
 // blocks of 32 query rows (two at d=64, one at d=128); the K/V tiles in LDS
 // are shared by all eight.
 //   * Two wave groups run anti-phased.  Every wave alternates a matrix step
-//     (score MFMAs of one 32-key subtile, P·V MFMAs of the previous one) and
-//     a vector step (mask, row max, exponentials and packing of a subtile,
-//     plus the LDS reads that feed the next matrix step).  Group 1 runs one
-//     step behind group 0 and every step ends at a workgroup barrier, so on
-//     each SIMD one wave keeps the matrix core busy while its partner does the
-//     softmax arithmetic -- the two units overlap instead of taking turns.
+//     (score MFMAs of one 32-key subtile, P·V MFMAs of the previous one, and
+//     between them the LDS reads of the K and V operands of the next matrix
+//     step) and a vector step (mask, row max, exponentials and packing of a
+//     subtile, and the tile transfers).  Group 1 runs one step behind group 0
+//     and every step ends at a workgroup barrier, so on each SIMD one wave
+//     keeps the matrix core busy while its partner does the softmax
+//     arithmetic -- the two units overlap instead of taking turns.  The
+//     vector step is the longer of the two, so it carries no operand reads.
 //   * Q rows sit in registers as the B operand of 32x32x16 MFMA.
 //   * K and V tiles of 64 keys go from HBM/L2 straight into LDS with
 //     buffer-load-to-LDS (rows past the sequence end read as 0), into one of
@@ -120,10 +122,10 @@ __device__ __forceinline__ void wait_vm() {
 // End of a step: a workgroup barrier that nothing is scheduled across.  No
 // memory fence: buffer-to-LDS loads in flight stay in flight, their
 // completion is awaited explicitly.  A vector step also waits for this wave's
-// LDS reads, its own and those of the matrix step before it, so that once the
-// barrier opens nothing this wave read can still be pending when a later tile
-// fetch overwrites it; a matrix step leaves its reads in flight and goes
-// straight to the barrier.
+// LDS reads (those of the matrix step before it), so that once the barrier
+// opens nothing this wave read can still be pending when a later tile fetch
+// overwrites it; a matrix step leaves its reads in flight and goes straight
+// to the barrier.
 template <bool WAIT_LDS>
 __device__ __forceinline__ void step_end() {
   __builtin_amdgcn_sched_barrier(0);  // keep the wait below the step's own work
@@ -392,7 +394,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int e = 0; e < 16; ++e) oacc[blk][dt][e] = 0.f;
   }
 
-  // Operands staged in registers one step ahead of the matrix step that uses them.
+  // Operands read during the matrix step before the one that uses them.
   u32x4 kf[KK];      // K of the next score subtile
   u32x4 vf[DT][2];   // V of the next P·V subtile, per output tile and 16-key k-step
   f32x16 s[NB];      // scores of one subtile: s[blk][e] is key 16·(e>>3) + 8·half + (e&7)
@@ -436,6 +438,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
       for (int blk = 0; blk < NB; ++blk) s[blk] = T::mfma32(kf[kk], qf[blk][kk], s[blk]);
+  };
+
+  // scores of the staged K operand while the K operand of subtile sb of the
+  // tile in buffer stg is read into the same registers, each after its last use
+  auto qk_load_k = [&](auto stg, int sb) ATTN_INLINE {
+    const char* st = subtile(stg, sb);
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[blk][e] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk) s[blk] = T::mfma32(kf[kk], qf[blk][kk], s[blk]);
+      kf[kk] = lds_read16(st, k_rd[kk]);
+      __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
   };
 
   auto pv = [&]() ATTN_INLINE {
@@ -591,24 +611,25 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
 
   // ---- the steps of one wave, for subtiles u = 2t (sb 0) and 2t+1 (sb 1) of tile t:
-  //   step 0      matrix  scores of subtile 0 (K read here); read V of 0
-  //   step 4t+1   vector  softmax of 2t;   read K of 2t+1
-  //   step 4t+2   matrix  scores of 2t+1, P·V of 2t;   read V of 2t+1
-  //   step 4t+3   vector  softmax of 2t+1; read K of 2t+2
-  //   step 4t+4   matrix  scores of 2t+2, P·V of 2t+1; read V of 2t+2
-  // so each group's LDS reads are split evenly between its two kinds of step,
-  // and tile t is read by steps 4t-1 .. 4t+2 (0 .. 2 for tile 0).  Every step
-  // ends at a workgroup barrier.  Group 1 passes one extra barrier first, so it
-  // runs each step one phase after group 0: on every SIMD one wave is in a
-  // matrix step while the other is in a vector step.
+  //   step 0      matrix  scores of subtile 0 (K of 0 read first); read K of 1, V of 0
+  //   step 4t+1   vector  softmax of 2t
+  //   step 4t+2   matrix  scores of 2t+1, P·V of 2t;   read K of 2t+2, V of 2t+1
+  //   step 4t+3   vector  softmax of 2t+1
+  //   step 4t+4   matrix  scores of 2t+2, P·V of 2t+1; read K of 2t+3, V of 2t+2
+  // Each operand is read into its registers right after the MFMA that last
+  // used them, so the reads overlap the MFMAs; tile t is read by steps
+  // 4t-2 .. 4t+2 (0 .. 2 for tile 0).  Every step ends at a workgroup barrier.
+  // Group 1 passes one extra barrier first, so it runs each step one phase
+  // after group 0: on every SIMD one wave is in a matrix step while the other
+  // is in a vector step.
   //
   // Tiles 0 .. S-1 are fetched up front.  Tile t+S-1 (t >= 1) is fetched at the
   // start of vector steps 4t+1 and 4t+3, half of its transfers each; its buffer
   // last held tile t-1, whose final read (group 1, step 4t-2) has returned by
   // the end of group 1's vector step 4t-1, i.e. before the barrier that opens
   // group 0's step 4t+1.  Each wave waits for its transfers of tile t+1 at the
-  // end of step 4t+1, before the barriers that precede group 0's first read of
-  // it (step 4t+3).
+  // end of step 4t, before the barriers that precede group 0's first read of
+  // it (step 4t+2).
   static_assert(S >= 3, "the fetch schedule needs three tile buffers");
   static_assert(PT % 2 == 0 && PT <= 4, "transfers split evenly over the two vector steps of a tile");
   fetch_tile();
@@ -620,8 +641,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (grp == 1) step_end<true>();
 
   load_k(std::integral_constant<int, 0>{}, 0);
-  qk();
+  qk_load_k(std::integral_constant<int, 0>{}, 1);
   load_v(std::integral_constant<int, 0>{}, 0);
+  if (nkt > 1) wait_tile(1);
   pin_matrix_step();
   step_end<false>();
   // Transfers of the tile being fetched, issued at the start of a vector step
@@ -639,30 +661,28 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   auto tile_steps = [&](int t, auto stg, auto last_tag) ATTN_INLINE {
     constexpr bool LAST = decltype(last_tag)::value;
     const bool fetch = t >= 1 && t + S - 1 < nkt;
-    // step 4t+1: softmax of subtile 2t; K of 2t+1
+    // step 4t+1: softmax of subtile 2t
     fetch_half(fetch, 0);
-    load_k(stg, 1);
     softmax(key0 + 64 * t);
-    if (!LAST) wait_tile(t + 1);
     pin_vector_step();
     step_end<true>();
-    // step 4t+2: scores of 2t+1, P·V of 2t; V of 2t+1
-    qk();
+    // step 4t+2: scores of 2t+1, P·V of 2t; K of 2t+2, V of 2t+1
+    if (LAST) qk(); else qk_load_k(next_stage(stg), 0);
     pv_then_load_v(stg, 1);
     pin_matrix_step();
     step_end<false>();
-    // step 4t+3: softmax of 2t+1; K of 2t+2
+    // step 4t+3: softmax of 2t+1
     fetch_half(fetch, 1);
-    if (!LAST) load_k(next_stage(stg), 0);
     softmax(key0 + 64 * t + 32);
     pin_vector_step();
     step_end<true>();
-    // step 4t+4: scores of 2t+2, P·V of 2t+1; V of 2t+2
+    // step 4t+4: scores of 2t+2, P·V of 2t+1; K of 2t+3, V of 2t+2; tile t+2 landed
     if (LAST) {
       pv();
     } else {
-      qk();
+      qk_load_k(next_stage(stg), 1);
       pv_then_load_v(next_stage(stg), 0);
+      if (t + 2 < nkt) wait_tile(t + 2);
     }
     pin_matrix_step();
     step_end<false>();
