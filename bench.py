@@ -16,7 +16,9 @@ untimed warm-up steps.  ``value`` is the prefill throughput in algorithmic
 TFLOP/s (4·d FLOPs per visible query-key pair); the decode throughput in
 algorithmic KV GB/s (every K and V byte read once) is reported beside it.  Each
 kernel's average launch duration is taken with HIP events recorded on the
-stream the kernels are launched on; the ``roofline`` object is for the
+stream the kernels are launched on, around the launches of every fifth timed
+step (an event pair around every launch would add about 10 µs of stream
+overhead to each decode step's wall clock); the ``roofline`` object is for the
 dominant (longest-running) kernel, ``kernels`` lists all of them.  Inputs
 alternate between two copies so no launch finds the previous one's data in the
 last-level cache.
@@ -58,6 +60,7 @@ PEAK_HBM_GBS = 8000.0            # MI355X HBM3E peak
 PREFILL = ["prefill_b4_h32_n4096_d64_bf16", "prefill_b4_h32_n4096_d128_bf16"]
 DECODE = "decode_b1_hq32_hkv8_d128_len262144_bf16"
 PAGE_SIZE = 16
+EVENT_EVERY = 5                  # timed steps whose launches are bracketed by HIP events
 APPEND = "append_causal_b16_hq32_hkv8_d128_q256to2048_past0to16384_bf16"
 CSRC = os.path.join(ROOT, "exact_attention_flashattention_amd", "csrc")
 KERNEL_SOURCES = {
@@ -305,6 +308,9 @@ def main() -> int:
     def events(n):
         return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
+    def timed_with_events():
+        return range(0, K, EVENT_EVERY)
+
     result_kernels = []
     pre_wall = dec_wall = 0.0
     pre_flops = sum(w.flops() for w, _, _ in pre)
@@ -314,14 +320,14 @@ def main() -> int:
         for i in range(W):
             prefill_step(i)
         torch.cuda.synchronize()
-        ev = [[events(2) for _ in pre] for _ in range(K)]
+        ev = {i: [events(2) for _ in pre] for i in timed_with_events()}
         t0 = time.perf_counter()
         for i in range(K):
-            prefill_step(i, ev[i])
+            prefill_step(i, ev.get(i))
         torch.cuda.synchronize()
         pre_wall = time.perf_counter() - t0
         for j, (w, _, outs) in enumerate(pre):
-            ms = sum(ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(K)) / K
+            ms = sum(e[j][0].elapsed_time(e[j][1]) for e in ev.values()) / len(ev)
             tflops = w.flops() / (ms * 1e-3) / 1e12
             if not torch.isfinite(outs[0]).all():
                 raise RuntimeError(f"non-finite prefill output on {w.name}")
@@ -338,17 +344,17 @@ def main() -> int:
         for i in range(W):
             decode_step(i)
         torch.cuda.synchronize()
-        ev = [events(3) for _ in range(K)]
+        ev = {i: events(3) for i in timed_with_events()}
         t0 = time.perf_counter()
         for i in range(K):
-            decode_step(i, ev[i])
+            decode_step(i, ev.get(i))
         torch.cuda.synchronize()
         dec_wall = time.perf_counter() - t0
         if not torch.isfinite(out).all():
             raise RuntimeError("non-finite decode output")
         kv_bytes = w.kv_bytes(total_len)
-        ms_split = sum(e[0].elapsed_time(e[1]) for e in ev) / K
-        ms_merge = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+        ms_split = sum(e[0].elapsed_time(e[1]) for e in ev.values()) / len(ev)
+        ms_merge = sum(e[1].elapsed_time(e[2]) for e in ev.values()) / len(ev)
         gbs = kv_bytes / (ms_split * 1e-3) / 1e9
         result_kernels.append({
             "kernel": "decode_splitk_kernel<bf16,d128>", "workload": w.name, "avg_ms": ms_split, "bound": "hbm",
@@ -371,16 +377,16 @@ def main() -> int:
         for i in range(W):
             paged_step(i)
         torch.cuda.synchronize()
-        ev = [events(3) for _ in range(K)]
+        ev = {i: events(3) for i in timed_with_events()}
         t0 = time.perf_counter()
         for i in range(K):
-            paged_step(i, ev[i])
+            paged_step(i, ev.get(i))
         torch.cuda.synchronize()
         pag_wall = time.perf_counter() - t0
         if not torch.isfinite(out).all():
             raise RuntimeError("non-finite paged decode output")
         kv_bytes = w.kv_bytes(total_len)
-        ms_split = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+        ms_split = sum(e[0].elapsed_time(e[1]) for e in ev.values()) / len(ev)
         gbs = kv_bytes / (ms_split * 1e-3) / 1e9
         label = f"decode_splitk_kernel<bf16,d128,paged{PAGE_SIZE}>"
         result_kernels.append({
@@ -399,16 +405,16 @@ def main() -> int:
         for i in range(W):
             append_step(i)
         torch.cuda.synchronize()
-        ev = [events(2) for _ in range(K)]
+        ev = {i: events(2) for i in timed_with_events()}
         t0 = time.perf_counter()
         for i in range(K):
-            append_step(i, ev[i])
+            append_step(i, ev.get(i))
         torch.cuda.synchronize()
         app_wall = time.perf_counter() - t0
         if not torch.isfinite(outs[0]).all():
             raise RuntimeError("non-finite append output")
         flops = w.flops(nq, nk)
-        ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+        ms = sum(e[0].elapsed_time(e[1]) for e in ev.values()) / len(ev)
         tflops = flops / (ms * 1e-3) / 1e12
         label = "prefill_fwd_kernel<bf16,d128,causal,varlen>"
         result_kernels.append({
@@ -428,16 +434,16 @@ def main() -> int:
         for i in range(W):
             q4_step(i)
         torch.cuda.synchronize()
-        ev = [events(3) for _ in range(K)]
+        ev = {i: events(3) for i in timed_with_events()}
         t0 = time.perf_counter()
         for i in range(K):
-            q4_step(i, ev[i])
+            q4_step(i, ev.get(i))
         torch.cuda.synchronize()
         q4_wall = time.perf_counter() - t0
         if not torch.isfinite(out).all():
             raise RuntimeError("non-finite 4-bit decode output")
         q4_bytes = 2.0 * w.hkv * total_len * (w.d // 2 + 4)  # codes + one fp32 scale per row, K and V
-        ms_split = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+        ms_split = sum(e[0].elapsed_time(e[1]) for e in ev.values()) / len(ev)
         gbs = q4_bytes / (ms_split * 1e-3) / 1e9
         label = "decode_q4_kernel<bf16,d128,rotated>"
         result_kernels.append({
