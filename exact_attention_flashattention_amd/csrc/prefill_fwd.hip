@@ -136,6 +136,15 @@ __device__ __forceinline__ void step_end() {
   asm volatile("" ::: "memory");
 }
 
+// A wave-uniform pointer placed in scalar registers (the compiler may have
+// computed it with vector instructions, e.g. through an integer division).
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  return (const char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Kernel-local helpers are lambdas; all of them are inlined (a call would
 // spill the operand registers to scratch memory).
 #define ATTN_INLINE __attribute__((always_inline))
@@ -314,11 +323,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int GROUP_ROWS = Cfg::WAVES * 1024 / ROWB;  // rows of one transfer group
   constexpr int PT = 2 * Cfg::DMA;  // transfers per tile per wave: part j is tensor j&1 (K, V), group j>>1
   // Fetch cursor: scalar state of the next tile to fetch, advanced one tile at a
-  // time so that issuing a transfer costs a handful of scalar instructions.
+  // time so that issuing a transfer costs a handful of scalar instructions (its
+  // values are moved to scalar registers explicitly; left to the compiler, parts
+  // of it live in vector registers and every transfer pays for the moves).
   int issued = 0;                                       // transfers this wave has issued so far
-  const char* f_k = kp + (size_t)key0 * kv_stride;      // K row j0 of the cursor's tile
-  const char* f_v = vp + (size_t)key0 * kv_stride;      // V row j0
-  uint32_t f_rem = (uint32_t)(nk - key0) * kv_stride;   // bytes from row j0 to the sequence end
+  const char* f_k = uniform_ptr(kp + (size_t)key0 * kv_stride);  // K row j0 of the cursor's tile
+  const char* f_v = uniform_ptr(vp + (size_t)key0 * kv_stride);  // V row j0
+  uint32_t f_rem = (uint32_t)__builtin_amdgcn_readfirstlane(     // bytes from row j0 to the sequence end
+      (int)((uint32_t)(nk - key0) * kv_stride));
   const uint32_t f_dst0 = lds_addr(lds) + wave * 1024;  // this wave's transfers land at stage + g·1024
   uint32_t f_dst = f_dst0;                              // ... of the cursor's stage
   auto fetch_part = [&](int j) ATTN_INLINE {                        // transfer j of the cursor's tile
@@ -333,7 +345,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const uint32_t step = Cfg::BC * kv_stride;
     f_k += step;
     f_v += step;
-    f_rem = f_rem > step ? f_rem - step : 0u;
+    f_rem = (uint32_t)__builtin_amdgcn_readfirstlane((int)(f_rem > step ? f_rem - step : 0u));
     f_dst = f_dst + Cfg::TILE == f_dst0 + S * Cfg::TILE ? f_dst0 : f_dst + Cfg::TILE;
   };
   auto fetch_tile = [&]() ATTN_INLINE {
@@ -504,14 +516,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // 2^8 and the row maximum is at most 8 above the
   // reference, so nothing overflows or loses precision; o and l share the
   // reference, so o/l is the same either way.
+  // The row sum is accumulated in two dot2 chains, one of them starting from
+  // l itself (measured: 1 % faster than four chains added to l afterwards).
+  constexpr int NCH = 2;
   float neg_ref[NB], lim[NB];  // -m_run (0 while m_run = -inf); the row-sum limit (-1 forces a raise)
 #pragma unroll
   for (int blk = 0; blk < NB; ++blk) {
     neg_ref[blk] = 0.f;
     lim[blk] = -1.f;
   }
-  auto probs = [&](int blk, float nref) ATTN_INLINE {  // returns this lane's sum of the 16 rounded probabilities
-    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+  auto probs = [&](int blk, float nref, float acc) ATTN_INLINE {  // acc + this lane's 16 rounded probabilities
+    float ps[NCH];
+    ps[0] = acc;
+#pragma unroll
+    for (int i = 1; i < NCH; ++i) ps[i] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -519,9 +537,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const float a0 = fast_exp2(fmaf(s[blk][8 * ks + 2 * i], c, nref));
         const float a1 = fast_exp2(fmaf(s[blk][8 * ks + 2 * i + 1], c, nref));
         pf[blk][ks][i] = T::pack2(a0, a1);
-        ps[i] = T::add_pair(ps[i], pf[blk][ks][i]);
+        ps[(4 * ks + i) % NCH] = T::add_pair(ps[(4 * ks + i) % NCH], pf[blk][ks][i]);
       }
-    return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    float r = ps[0];
+#pragma unroll
+    for (int i = 1; i < NCH; ++i) r += ps[i];
+    return r;
   };
   auto softmax = [&](int s0) ATTN_INLINE {
     if (s0 + 32 > nk || (CAUSAL && s0 + 31 > qw + off) ||
@@ -557,12 +578,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int e = 0; e < 16; ++e) s[blk][e] += fmaf(alibi_raw, (float)(16 * (e >> 3) + (e & 7)), base);
       }
     }
-    float psum[NB];
+    float lnew[NB];
     bool grow = false;
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
-      psum[blk] = probs(blk, neg_ref[blk]);
-      grow |= !(psum[blk] <= lim[blk]);  // also true for an infinite or NaN sum
+      lnew[blk] = probs(blk, neg_ref[blk], l_run[blk]);
+      grow |= !(lnew[blk] - l_run[blk] <= lim[blk]);  // the subtile's sum; also true if infinite or NaN
     }
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
@@ -581,11 +602,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         m_run[blk] = m_new;
         neg_ref[blk] = -ref;
         lim[blk] = m_new == kNegInf ? -1.f : kRescaleSum;
-        psum[blk] = probs(blk, -ref);
+        lnew[blk] = probs(blk, -ref, l_run[blk]);
       }
     }
 #pragma unroll
-    for (int blk = 0; blk < NB; ++blk) l_run[blk] += psum[blk];
+    for (int blk = 0; blk < NB; ++blk) l_run[blk] = lnew[blk];
   };
 
   // results of a vector step (probabilities and running statistics) and of a
