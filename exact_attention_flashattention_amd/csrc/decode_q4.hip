@@ -233,7 +233,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const uint32_t v_off = (uint32_t)vrow * RB + (lane & 1) * (RB / 2);   // VB = RB/2 bytes per lane
 
   auto load = [&](Q4Stage<D>& st, int k0) {
-    const uint32_t rows = (uint32_t)(end - k0);
+    const uint32_t rows = k0 < end ? (uint32_t)(end - k0) : 0u;  // past the end: reads nothing
     const bufres rk = make_bufres(kbase + (size_t)k0 * RB, rows * RB);
     const bufres rv = make_bufres(vbase + (size_t)k0 * RB, rows * RB);
     const bufres rks = make_bufres(ksbase + k0, rows * 4);
@@ -342,16 +342,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   // A ring of kQDepth steps: while step i is processed, steps i+1 .. i+kQDepth-1
   // are in flight (a 4-bit step is a quarter of a 16-bit one, so one step ahead
   // leaves the wave waiting on memory latency).
+  // The loads are issued unconditionally (past the end they read nothing), so
+  // the compiler can count the steps in flight and wait for the current one only.
   Q4Stage<D> st[kQDepth];
 #pragma unroll
-  for (int i = 0; i + 1 < kQDepth; ++i)
-    if (start + i * kQStep < end) load(st[i], start + i * kQStep);
+  for (int i = 0; i + 1 < kQDepth; ++i) load(st[i], start + i * kQStep);
   bool done = false;
   for (int k0 = start; !done; k0 += kQDepth * kQStep) {
 #pragma unroll
     for (int i = 0; i < kQDepth; ++i) {
       const int ahead = k0 + (i + kQDepth - 1) * kQStep;
-      if (ahead < end) load(st[(i + kQDepth - 1) % kQDepth], ahead);
+      load(st[(i + kQDepth - 1) % kQDepth], ahead);
       process(st[i], k0 + i * kQStep);
       if (k0 + (i + 1) * kQStep >= end) {
         done = true;

@@ -194,7 +194,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       for (int i = 0; i < VCH; ++i)
         st.v[i] = bload16(rv[i / VHALF], v_off[i] - (uint32_t)(i / VHALF) * 16 * D * 2);
     } else {
-      const uint32_t bytes = (uint32_t)(end - k0) * D * 2;
+      const uint32_t bytes = k0 < end ? (uint32_t)(end - k0) * D * 2 : 0u;  // past the end: reads nothing
       const bufres rk = make_bufres(kbase + (size_t)k0 * D * 2, bytes);
       const bufres rv = make_bufres(vbase + (size_t)k0 * D * 2, bytes);
 #pragma unroll
@@ -278,17 +278,19 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     }
   };
 
+  // The next step's loads are issued unconditionally (past the end they read
+  // nothing): with a conditional load the compiler cannot count the loads in
+  // flight and waits for all of them, the next step's included, before using
+  // the current step's registers.
   DecodeStage<D> A, B;
   load(A, start);
   for (int k0 = start;; k0 += 2 * kStep) {
-    const bool more1 = k0 + kStep < end;
-    if (more1) load(B, k0 + kStep);
+    load(B, k0 + kStep);
     process(A, k0);
-    if (!more1) break;
-    const bool more2 = k0 + 2 * kStep < end;
-    if (more2) load(A, k0 + 2 * kStep);
+    if (k0 + kStep >= end) break;
+    load(A, k0 + 2 * kStep);
     process(B, k0 + kStep);
-    if (!more2) break;
+    if (k0 + 2 * kStep >= end) break;
   }
 
   // partial state of this slice, natural-log units
