@@ -33,6 +33,12 @@ They are reported beside the step (``decode_paged``, ``append``,
 ``decode_q4`` and in ``kernels``) and are not part of ``value`` or
 ``ms_per_step``.
 
+``measured_ceilings`` gives two rates measured on the same GPU in the same
+run, with the library's measurement helpers (``include/attn_calibrate.h``): a
+back-to-back bf16 MFMA loop and a streaming read of a 1 GiB buffer; each
+kernel in ``kernels`` also carries ``frac_of_measured``, its rate against the
+ceiling of its bound (``frac`` stays the fraction of the published peak).
+
 ``cpu_baseline`` times the fp64 oracle on a bounded sample of the same prefill
 workload (whole heads until about ``--cpu-seconds`` have passed), on the host
 cores, as a reported baseline only.
@@ -144,6 +150,40 @@ def cpu_baseline(inputs, w, seconds: float):
                       f"{elapsed:.1f} s; host {cpu_model()}, {os.cpu_count()} logical CPUs"}
 
 
+def measured_ceilings(torch, lib, check, stream, reps: int = 10) -> dict:
+    """Sustained bf16 MFMA rate and HBM read rate on this GPU (median of timed calls)."""
+    blocks, iters = 512, 4096                      # two workgroups per CU on 256 CUs
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB, far beyond the caches
+    scratch = torch.empty(4096, dtype=torch.uint8, device="cuda")
+    read_blocks = (2048, 4096, 8192)
+    sp = stream.cuda_stream
+
+    def timed(launch):
+        for _ in range(3):
+            launch()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            launch()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return sorted(ts)[len(ts) // 2]
+
+    ms_mfma = timed(lambda: check("attn_calib_mfma_bf16", lib.attn_calib_mfma_bf16(out.data_ptr(), blocks, iters, sp)))
+    nbytes = buf.numel() * 4
+    ms_read = min(timed(lambda rb=rb: check("attn_calib_read", lib.attn_calib_read(buf.data_ptr(), nbytes,
+                                                                                   scratch.data_ptr(), rb, sp)))
+                  for rb in read_blocks)
+    flops = blocks * 4 * iters * 4 * 32768
+    return {"mfma_bf16_tflops": flops / (ms_mfma * 1e-3) / 1e12, "hbm_read_gbs": nbytes / (ms_read * 1e-3) / 1e9,
+            "how": f"attn_calib_mfma_bf16 ({blocks} workgroups x {iters} rounds of 4 MFMA chains) and "
+                   f"attn_calib_read (1 GiB, best of {'/'.join(map(str, read_blocks))} workgroups); "
+                   f"median of {reps} timed calls each"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -151,6 +191,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the measured MFMA-loop and streaming-read ceilings")
     ap.add_argument("--only", choices=["all", "prefill_d64", "prefill_d128", "decode", "decode_paged", "append", "decode_q4"], default="all",
                     help="run only one kernel family (for profiler runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -491,6 +532,15 @@ def main() -> int:
         "roofline": roofline,
         "kernels": result_kernels,
     }
+
+    if args.only == "all" and not args.no_ceilings:
+        ceil = measured_ceilings(torch, A._lib.load(), A._lib.check, stream)
+        line["measured_ceilings"] = ceil
+        for r in result_kernels:
+            top = ceil["mfma_bf16_tflops"] if r["bound"] == "mfma" else ceil["hbm_read_gbs"]
+            r["frac_of_measured"] = r["achieved"] / top
+    else:
+        line["measured_ceilings"] = None
 
     if pre and not args.no_cpu_baseline:
         w, copies, _ = pre[-1]

@@ -17,7 +17,8 @@ import torch  # noqa: F401  (load torch's HIP runtime before the library)
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libattn.so")
-HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "attn.h")
+INCLUDE_DIR = os.path.join(os.path.dirname(PKG_DIR), "include")
+HEADER_PATH = os.path.join(INCLUDE_DIR, "attn.h")
 
 STATUS_NAMES = {
     0: "ATTN_OK",
@@ -50,6 +51,9 @@ SIGNATURES = {
                                        _c_int, _c_float, _c_int, _c_int, _vp, _vp, _vp, _vp]),
     "attn_kv_quantize_q4": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _c_int, _vp, _vp, _vp]),
     "attn_merge_partials": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _c_int, _vp]),
+    # measurement helpers (include/attn_calibrate.h)
+    "attn_calib_mfma_bf16": (_c_int, [_vp, _c_int, _c_int, _vp]),
+    "attn_calib_read": (_c_int, [_vp, _c_size, _vp, _c_int, _vp]),
 }
 
 
@@ -60,11 +64,15 @@ class AttnError(RuntimeError):
         super().__init__(f"{fn} returned {self.status_name}")
 
 
-def header_functions(path: str = HEADER_PATH):
-    """Names of the functions ``include/attn.h`` declares."""
-    text = open(path).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)
+def header_functions(paths=None):
+    """Names of the functions the headers under ``include/`` declare."""
+    if paths is None:
+        paths = sorted(os.path.join(INCLUDE_DIR, f) for f in os.listdir(INCLUDE_DIR) if f.endswith(".h"))
+    names = []
+    for path in paths:
+        text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+        names += re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)
+    return names
 
 
 _LIB = None

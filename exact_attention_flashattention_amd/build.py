@@ -18,7 +18,8 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libattn.so")
 
-SOURCES = ["attn_abi.hip", "merge_partials.hip", "decode_splitk.hip", "decode_q4.hip", "quantize_q4.hip", "prefill_fwd.hip"]
+SOURCES = ["attn_abi.hip", "merge_partials.hip", "decode_splitk.hip", "decode_q4.hip", "quantize_q4.hip", "prefill_fwd.hip",
+           "calibrate.hip"]
 
 HIPCC_FLAGS = [
     "-std=c++17",

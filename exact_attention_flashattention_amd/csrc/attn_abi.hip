@@ -1,4 +1,4 @@
-// C ABI of libattn.so (declared in include/attn.h): argument validation on
+// C ABI of libattn.so (declared in include/attn.h and include/attn_calibrate.h): argument validation on
 // the host, split planning for decode, and dispatch to the kernel launchers.
 // Nothing here allocates, frees or synchronises device memory.
 #include <cmath>
@@ -6,6 +6,7 @@
 #include <cstdlib>
 
 #include "attn.h"
+#include "attn_calibrate.h"
 #include "launchers.hpp"
 
 namespace {
@@ -208,6 +209,20 @@ attn_status attn_merge_partials(const float* part_m, const float* part_l, const 
   if (!aligned16(part_o) || !aligned16(o)) return ATTN_ERR_MISALIGNED;
   return from_hip(attn::launch_merge(part_m, part_l, part_o, batch * hq, d, num_splits, out_dtype == ATTN_BF16, o,
                                      static_cast<hipStream_t>(stream)));
+}
+
+attn_status attn_calib_mfma_bf16(float* out, int blocks, int iters, void* stream) {
+  if (!out) return ATTN_ERR_NULL_PTR;
+  if (blocks < 1 || blocks > (1 << 20) || iters < 1 || iters > (1 << 24)) return ATTN_ERR_BAD_SHAPE;
+  if (!aligned16(out)) return ATTN_ERR_MISALIGNED;
+  return from_hip(attn::launch_calib_mfma(out, blocks, iters, static_cast<hipStream_t>(stream)));
+}
+
+attn_status attn_calib_read(const void* buf, size_t bytes, void* scratch, int blocks, void* stream) {
+  if (!buf || !scratch) return ATTN_ERR_NULL_PTR;
+  if (bytes == 0 || bytes % 16 != 0 || blocks < 1 || blocks > (1 << 20)) return ATTN_ERR_BAD_SHAPE;
+  if (!aligned16(buf) || !aligned16(scratch)) return ATTN_ERR_MISALIGNED;
+  return from_hip(attn::launch_calib_read(buf, bytes, scratch, blocks, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

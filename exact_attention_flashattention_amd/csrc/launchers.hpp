@@ -46,4 +46,8 @@ hipError_t launch_quantize_q4(const void* x, int rows, int d, bool bf16, bool ro
 hipError_t launch_merge(const float* part_m, const float* part_l, const float* part_o, int rows, int d,
                         int num_splits, bool bf16, void* out, hipStream_t stream);
 
+// Measurement helpers (calibrate.hip): a bf16 MFMA loop and a streaming read.
+hipError_t launch_calib_mfma(float* out, int blocks, int iters, hipStream_t stream);
+hipError_t launch_calib_read(const void* buf, size_t bytes, void* scratch, int blocks, hipStream_t stream);
+
 }  // namespace attn

@@ -1,5 +1,6 @@
 """The C ABI on the host (CPU only): the library loads, exports every function
-include/attn.h declares, and rejects bad arguments before launching anything.
+the headers under include/ declare, and rejects bad arguments before
+launching anything.
 
 Every call here fails validation (or is a pure host helper), so no kernel is
 ever launched and no device is touched.
@@ -24,7 +25,8 @@ def lib():
 
 def test_library_exports_every_declared_function(lib):
     names = _lib.header_functions()
-    assert set(names) == set(_lib.SIGNATURES), "binding signatures out of sync with include/attn.h"
+    assert "attn_calib_read" in names and "attn_prefill_fwd" in names
+    assert set(names) == set(_lib.SIGNATURES), "binding signatures out of sync with include/*.h"
     raw = ctypes.CDLL(_lib.LIB_PATH)
     for name in names:
         assert hasattr(raw, name), name
@@ -196,3 +198,16 @@ def test_no_cpu_fallback_in_binding():
             assert "scaled_dot_product_attention" not in src
             for call in ("softmax(", ".exp(", "matmul", "bmm(", "einsum"):
                 assert call not in src, (fn, call)
+
+
+def test_calibration_helpers_reject_bad_arguments(lib):
+    assert lib.attn_calib_mfma_bf16(None, 512, 16, None) == NULL
+    for blocks, iters in ((0, 16), (-1, 16), ((1 << 20) + 1, 16), (512, 0), (512, (1 << 24) + 1)):
+        assert lib.attn_calib_mfma_bf16(P, blocks, iters, None) == SHAPE, (blocks, iters)
+    assert lib.attn_calib_mfma_bf16(P + 4, 512, 16, None) == MISAL
+    assert lib.attn_calib_read(None, 1 << 20, P, 64, None) == NULL
+    assert lib.attn_calib_read(P, 1 << 20, None, 64, None) == NULL
+    for nbytes, blocks in ((0, 64), (17, 64), (1 << 20, 0), (1 << 20, (1 << 20) + 1)):
+        assert lib.attn_calib_read(P, nbytes, P, blocks, None) == SHAPE, (nbytes, blocks)
+    assert lib.attn_calib_read(P + 8, 1 << 20, P, 64, None) == MISAL
+    assert lib.attn_calib_read(P, 1 << 20, P + 8, 64, None) == MISAL
