@@ -89,6 +89,51 @@ def test_prefill_causal_1head_512_fp16_full(A):
     assert torch.equal(out[0, 0, 0], v[0, 0, 0])
 
 
+def run_prefill_tensors(A, q, k, v, causal, scale, tag):
+    out = A.prefill_fwd(q, k, v, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    assert_close(out, oracle.attention(f64(q), f64(k), f64(v), scale, causal), tag)
+
+
+@pytest.mark.parametrize("d,dtype", [(64, "bf16"), (128, "bf16"), (128, "f16")])
+@pytest.mark.parametrize("causal", [False, True])
+def test_prefill_large_logits(A, d, dtype, causal):
+    """Q scaled by 8 (a power of two: exact after rounding): score spread ~8 in natural units, so
+    exponentials without a reference would overflow fp16 and the running reference is raised often."""
+    w = workloads.Prefill(f"prefill_large_logits_{d}_{dtype}", 1, 2, 1, 1000, d, causal, dtype)
+    announce(w.name)
+    q, k, v = workloads.prefill_inputs(w, device=DEV, salt=3)
+    run_prefill_tensors(A, q * 8, k, v, causal, w.scale, w.name)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_prefill_rising_scores_force_repeated_raises(A, d, causal):
+    """Key rows of 64-key tile t scaled by 1 + 2t: each tile's row maximum passes the previous one by
+    several units of log2, so the kernel raises its reference again and again along the row."""
+    w = workloads.Prefill(f"prefill_rising_{d}", 1, 2, 2, 1000, d, causal, "bf16")
+    announce(w.name)
+    q, k, v = workloads.prefill_inputs(w, salt=5)
+    growth = (1.0 + 2.0 * (torch.arange(w.n) // 64).float()).view(1, 1, -1, 1)
+    k = (k.float() * growth).to(k.dtype)
+    run_prefill_tensors(A, q.to(DEV), k.to(DEV), v.to(DEV), causal, w.scale, w.name)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_prefill_all_scores_far_below_zero(A, d, causal):
+    """Keys = u + small noise and q = -beta·u: every score is about -200 (natural units), far below
+    where exp underflows; softmax is shift-invariant, so only the noise decides the weights."""
+    w = workloads.Prefill(f"prefill_negative_{d}", 1, 2, 1, 700, d, causal, "bf16")
+    announce(w.name)
+    _, k0, v = workloads.prefill_inputs(w, salt=7)
+    u = k0[:, :, :1, :].float()                      # one key row as the common direction
+    k = (u + 0.1 * k0.float()).to(torch.bfloat16)
+    beta = 200.0 / float((u * u).sum()) / w.scale
+    q = (-beta * u).expand(-1, w.hq, w.n, -1).contiguous().to(torch.bfloat16)
+    run_prefill_tensors(A, q.to(DEV), k.to(DEV), v.to(DEV), causal, w.scale, w.name)
+
+
 @pytest.mark.parametrize("name", ["prefill_b4_h32_n4096_d64_bf16", "prefill_b4_h32_n4096_d128_bf16",
                                   "prefill_causal_gqa_b1_hq32_hkv8_n32768_d128_bf16"])
 def test_prefill_full_size_sampled_rows(A, name):
