@@ -1,0 +1,133 @@
+"""GPU parity on seeded random configurations, through the C ABI, against the
+fp64 oracle (same tolerance as test_gpu_parity: max|Δ| <= 2e-2, mean|Δ| <= 2e-3).
+
+Each case draws its shape, head layout, element type, masking and split count
+from a generator seeded by the case number, so a failure names a configuration
+that reruns identically.  Sizes stay small enough for the oracle.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from test_gpu_parity import assert_close, announce, f64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+HEADS = [(1, 1), (2, 1), (4, 2), (6, 3), (8, 1), (12, 4)]
+
+
+@pytest.fixture(scope="module")
+def A():
+    import exact_attention_flashattention_amd as A
+    A._lib.load()
+    return A
+
+
+def draw(case):
+    return np.random.default_rng(1_000_003 * case + 17)
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_random_prefill(A, case):
+    rng = draw(case)
+    hq, hkv = HEADS[rng.integers(len(HEADS))]
+    B, n = int(rng.integers(1, 3)), int(rng.integers(1, 901))
+    d = int(rng.choice([64, 128]))
+    causal, dtype = bool(rng.integers(2)), str(rng.choice(["bf16", "f16"]))
+    w = workloads.Prefill(f"random_prefill_{case}", B, hq, hkv, n, d, causal, dtype)
+    announce(f"{w.name}: B={B} hq={hq} hkv={hkv} n={n} d={d} causal={causal} {dtype}")
+    q, k, v = (t.to(DEV) for t in workloads.prefill_inputs(w))
+    out = A.prefill_fwd(q, k, v, causal=causal, scale=w.scale)
+    torch.cuda.synchronize()
+    assert_close(out, oracle.attention(f64(q), f64(k), f64(v), w.scale, causal), w.name)
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_random_varlen(A, case):
+    rng = draw(100 + case)
+    hq, hkv = HEADS[rng.integers(len(HEADS))]
+    d, dtype = int(rng.choice([64, 128])), str(rng.choice(["bf16", "f16"]))
+    causal = bool(rng.integers(4) > 0)
+    batch = int(rng.integers(1, 6))
+    nq = [int(x) for x in rng.integers(1, 600, batch)]
+    nk = [max(0, int(x) + (q if causal and rng.integers(3) else 0)) for x, q in zip(rng.integers(0, 900, batch), nq)]
+    if sum(nk) == 0:
+        nk[0] = 1  # at least one key row in the packed tensors
+    window = int(rng.choice([0, 0, 1, 33, 200, 5000])) if causal else 0
+    slopes = (torch.tensor(rng.uniform(0.01, 0.5, hq), dtype=torch.float32) if rng.integers(3) == 0 else None)
+    w = workloads.Varlen(f"random_varlen_{case}", batch, hq, hkv, d, causal, dtype, (1, 1), (0, 0))
+    announce(f"{w.name}: hq={hq} hkv={hkv} d={d} {dtype} causal={causal} window={window} "
+             f"alibi={slopes is not None} nq={nq} nk={nk}")
+    q, k, v, cu_q, cu_k = workloads.varlen_inputs(w, device=DEV, nq=nq, nk=nk)
+    out = A.prefill_varlen_fwd(q, k, v, cu_q.to(DEV), cu_k.to(DEV), max(nq), max(max(nk), 1), causal=causal,
+                               scale=w.scale, window=window,
+                               alibi_slopes=None if slopes is None else slopes.to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle.attention_varlen(f64(q), f64(k), f64(v), cu_q.numpy(), cu_k.numpy(), w.scale, causal,
+                                  window=window, alibi_slopes=None if slopes is None else slopes.double().numpy())
+    assert_close(out, ref, w.name)
+
+
+def random_decode_shape(rng):
+    hq, hkv = HEADS[rng.integers(len(HEADS))]
+    d, dtype = int(rng.choice([64, 128])), str(rng.choice(["bf16", "f16"]))
+    batch, max_len = int(rng.integers(1, 5)), int(rng.integers(1, 5000))
+    lens = torch.tensor(rng.integers(0, max_len + 1, batch), dtype=torch.int32)
+    splits = [None, 1, int(rng.integers(2, 40))][rng.integers(3)]
+    return hq, hkv, d, dtype, batch, max_len, lens, splits
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_random_decode(A, case):
+    rng = draw(200 + case)
+    hq, hkv, d, dtype, batch, max_len, lens, S = random_decode_shape(rng)
+    w = workloads.Decode(f"random_decode_{case}", batch, hq, hkv, d, max_len, None, float(rng.choice([1, 8])),
+                         dtype)
+    announce(f"{w.name}: B={batch} hq={hq} hkv={hkv} d={d} {dtype} L={max_len} lens={lens.tolist()} S={S} "
+             f"qx{w.q_mult}")
+    q, kc, vc, lens = workloads.decode_inputs(w, device=DEV, kv_lens=lens, max_kv_len=max_len, batch=batch)
+    out = A.decode(q, kc, vc, lens.to(DEV), S, w.scale)
+    torch.cuda.synchronize()
+    assert_close(out, oracle.decode(f64(q), f64(kc), f64(vc), lens.numpy(), w.scale), w.name)
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_random_paged_decode(A, case):
+    rng = draw(300 + case)
+    hq, hkv, d, dtype, batch, max_len, lens, S = random_decode_shape(rng)
+    page = int(rng.choice([16, 32, 64, 128]))
+    window = int(rng.choice([0, 0, 1, 40, 700]))
+    slopes = (torch.tensor(rng.uniform(0.01, 0.5, hq), dtype=torch.float32) if rng.integers(3) == 0 else None)
+    w = workloads.Decode(f"random_paged_{case}", batch, hq, hkv, d, max_len, None, 1.0, dtype)
+    announce(f"{w.name}: B={batch} hq={hq} hkv={hkv} d={d} {dtype} L={max_len} lens={lens.tolist()} S={S} "
+             f"page={page} window={window} alibi={slopes is not None}")
+    q, kc, vc, lens = workloads.decode_inputs(w, device=DEV, kv_lens=lens, max_kv_len=max_len, batch=batch)
+    kp, vp, table = workloads.paged_from_cache(kc, vc, lens, page, workloads.seed_for(w.name, "pages", 0),
+                                               spare_pages=int(rng.integers(0, 4)))
+    out = A.decode_paged(q, kp, vp, table.to(DEV), lens.to(DEV), S, w.scale, window=window,
+                         alibi_slopes=None if slopes is None else slopes.to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle.decode_paged(f64(q), f64(kp), f64(vp), table.numpy(), lens.numpy(), w.scale, window=window,
+                              alibi_slopes=None if slopes is None else slopes.double().numpy())
+    assert_close(out, ref, w.name)
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_random_q4_decode(A, case):
+    rng = draw(400 + case)
+    hq, hkv, d, dtype, batch, max_len, lens, S = random_decode_shape(rng)
+    rotated = bool(rng.integers(2))
+    w = workloads.Decode(f"random_q4_{case}", batch, hq, hkv, d, max_len, None, 1.0, dtype)
+    announce(f"{w.name}: B={batch} hq={hq} hkv={hkv} d={d} {dtype} L={max_len} lens={lens.tolist()} S={S} "
+             f"rotated={rotated}")
+    q, kq, ks, vq, vs, lens = workloads.decode_q4_inputs(w, rotated, device=DEV, kv_lens=lens, max_kv_len=max_len,
+                                                         batch=batch)
+    out = A.decode_q4(q, kq, ks, vq, vs, lens.to(DEV), rotated, S, w.scale)
+    torch.cuda.synchronize()
+    ref = oracle.decode_q4(f64(q), kq.cpu().numpy(), ks.cpu().double().numpy(), vq.cpu().numpy(),
+                           vs.cpu().double().numpy(), lens.numpy(), w.scale, rotated)
+    assert_close(out, ref, w.name)
