@@ -89,7 +89,7 @@ __device__ __forceinline__ u32x4 bload16(bufres r, uint32_t voffset) {
 
 // Buffer-load-to-LDS of 16 bytes per lane: lane i's bytes (from voffset in the
 // buffer described by `rsrc`, 0 past its end) land at LDS byte address
-// `lds_addr + 16·i`.  `lds_addr` must be wave-uniform.
+// `lds_base + OFF + 16·i`.  `lds_base` must be wave-uniform.
 //
 // Issued as inline assembly on purpose.  The compiler cannot tell which LDS
 // bytes a DMA writes, so after one it makes the next LDS read of ANY address
@@ -110,16 +110,18 @@ __device__ __forceinline__ i32x4 bufres_words(const void* base, uint32_t bytes) 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const ATTN_LDS char*)p;
 }
-__device__ __forceinline__ void dma16_to_lds(i32x4 rsrc, uint32_t voffset, uint32_t lds_byte_addr) {
+// The destination is `lds_base + OFF`, added straight into M0.
+template <uint32_t OFF>
+__device__ __forceinline__ void dma16_to_lds(i32x4 rsrc, uint32_t voffset, uint32_t lds_base) {
   // One wait state between the M0 write and the LDS-DMA that reads it.  M0 is
   // not listed as clobbered (the compiler rejects that for a reserved
   // register); the compiler itself writes M0 right before any instruction of
   // its own that reads it, so nothing it holds there lives across this one.
   asm volatile(
-      "s_mov_b32 m0, %2\n\t"
+      "s_add_u32 m0, %2, %3\n\t"
       "s_nop 0\n\t"
       "buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voffset),
-      "s"(rsrc), "s"(lds_byte_addr)
+      "s"(rsrc), "s"(lds_base), "n"(OFF)
       : "memory");
 }
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)

@@ -145,6 +145,15 @@ __device__ __forceinline__ const char* uniform_ptr(const char* p) {
   return (const char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
+// f(integral_constant<int, i>) for i = I .. N-1, each index a compile-time value.
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
 // Kernel-local helpers are lambdas; all of them are inlined (a call would
 // spill the operand registers to scratch memory).
 #define ATTN_INLINE __attribute__((always_inline))
@@ -323,22 +332,35 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int GROUP_ROWS = Cfg::WAVES * 1024 / ROWB;  // rows of one transfer group
   constexpr int PT = 2 * Cfg::DMA;  // transfers per tile per wave: part j is tensor j&1 (K, V), group j>>1
   // Fetch cursor: scalar state of the next tile to fetch, advanced one tile at a
-  // time so that issuing a transfer costs a handful of scalar instructions (its
-  // values are moved to scalar registers explicitly; left to the compiler, parts
-  // of it live in vector registers and every transfer pays for the moves).
+  // time.  The buffer resources of the tile's transfer groups (each from the
+  // group's first row to the sequence end, so rows past the end read as 0) are
+  // built when the cursor advances, so issuing a transfer costs an M0 write and
+  // the load itself.  (The values are moved to scalar registers explicitly;
+  // left to the compiler, parts of them live in vector registers and every
+  // transfer pays for the moves.)
   int issued = 0;                                       // transfers this wave has issued so far
   const char* f_k = uniform_ptr(kp + (size_t)key0 * kv_stride);  // K row j0 of the cursor's tile
   const char* f_v = uniform_ptr(vp + (size_t)key0 * kv_stride);  // V row j0
   uint32_t f_rem = (uint32_t)__builtin_amdgcn_readfirstlane(     // bytes from row j0 to the sequence end
       (int)((uint32_t)(nk - key0) * kv_stride));
+  i32x4 f_res[2][Cfg::DMA];  // [K, V][transfer group]
+  auto make_res = [&]() ATTN_INLINE {
+#pragma unroll
+    for (int g = 0; g < Cfg::DMA; ++g) {
+      const uint32_t src = g * GROUP_ROWS * kv_stride;  // the group's first byte in memory
+      const uint32_t rec = f_rem > src ? f_rem - src : 0u;
+      f_res[0][g] = bufres_words(f_k + src, rec);
+      f_res[1][g] = bufres_words(f_v + src, rec);
+    }
+  };
+  make_res();
   const uint32_t f_dst0 = lds_addr(lds) + wave * 1024;  // this wave's transfers land at stage + g·1024
   uint32_t f_dst = f_dst0;                              // ... of the cursor's stage
-  auto fetch_part = [&](int j) ATTN_INLINE {                        // transfer j of the cursor's tile
-    const uint32_t first = (j >> 1) * Cfg::WAVES * 1024;      // the transfer group's first byte in the tile
-    const uint32_t src = (j >> 1) * GROUP_ROWS * kv_stride;    // ... and in memory
-    const uint32_t rec = f_rem > src ? f_rem - src : 0u;      // rows past the end read as 0
-    dma16_to_lds(bufres_words(((j & 1) ? f_v : f_k) + src, rec), (j & 1) ? v_src : k_src,
-                 f_dst + (j & 1) * Cfg::VREG + first);
+  auto fetch_part = [&](auto j_tag) ATTN_INLINE {       // transfer j of the cursor's tile
+    constexpr int j = decltype(j_tag)::value;
+    // destination: the transfer group's first byte in the tile, in the tensor's region
+    dma16_to_lds<(j & 1) * Cfg::VREG + (j >> 1) * Cfg::WAVES * 1024>(f_res[j & 1][j >> 1], (j & 1) ? v_src : k_src,
+                                                                     f_dst);
     ++issued;
   };
   auto fetch_advance = [&]() ATTN_INLINE {
@@ -346,11 +368,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     f_k += step;
     f_v += step;
     f_rem = (uint32_t)__builtin_amdgcn_readfirstlane((int)(f_rem > step ? f_rem - step : 0u));
+    make_res();
     f_dst = f_dst + Cfg::TILE == f_dst0 + S * Cfg::TILE ? f_dst0 : f_dst + Cfg::TILE;
   };
   auto fetch_tile = [&]() ATTN_INLINE {
-#pragma unroll
-    for (int j = 0; j < PT; ++j) fetch_part(j);
+    static_for<0, PT>(fetch_part);
     fetch_advance();
   };
   // Wait until every transfer of tiles 0 .. t issued by this wave has landed:
@@ -668,14 +690,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   pin_matrix_step();
   step_end<false>();
   // Transfers of the tile being fetched, issued at the start of a vector step
-  // (measured: issued inside a matrix step they can hold up its MFMAs).
-  auto fetch_half = [&](bool fetch, int h) ATTN_INLINE {
+  // (measured: issued inside a matrix step they can hold up its MFMAs).  The
+  // cursor then advances in the matrix step after the second half, whose
+  // wave has time to spare at its barrier.
+  auto fetch_half = [&](bool fetch, auto h) ATTN_INLINE {
     __builtin_amdgcn_sched_barrier(0);
-    if (fetch) {
-#pragma unroll
-      for (int j = h * PT / 2; j < (h + 1) * PT / 2; ++j) fetch_part(j);
-      if (h == 1) fetch_advance();
-    }
+    if (fetch) static_for<decltype(h)::value * PT / 2, (decltype(h)::value + 1) * PT / 2>(fetch_part);
     __builtin_amdgcn_sched_barrier(0);
   };
   // one tile; the last one has no successor to read or score
@@ -683,7 +703,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr bool LAST = decltype(last_tag)::value;
     const bool fetch = t >= 1 && t + S - 1 < nkt;
     // step 4t+1: softmax of subtile 2t
-    fetch_half(fetch, 0);
+    fetch_half(fetch, std::integral_constant<int, 0>{});
     softmax(key0 + 64 * t);
     pin_vector_step();
     step_end<true>();
@@ -693,7 +713,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     pin_matrix_step();
     step_end<false>();
     // step 4t+3: softmax of 2t+1
-    fetch_half(fetch, 1);
+    fetch_half(fetch, std::integral_constant<int, 1>{});
     softmax(key0 + 64 * t + 32);
     pin_vector_step();
     step_end<true>();
@@ -703,7 +723,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     } else {
       qk_load_k(next_stage(stg), 1);
       pv_then_load_v(next_stage(stg), 0);
-      if (t + 2 < nkt) wait_tile(t + 2);
+      // tiles 0 .. min(t+3, nkt-1) are issued by now (tile t+3 during this tile's vector
+      // steps), so tile t+2 has landed once at most the PT·(S-3) transfers after it are in flight
+      if (t + 2 < nkt) {
+        if (t + S <= nkt) wait_vm<PT * (S - 3)>();
+        else wait_vm<0>();
+      }
+      if (fetch) fetch_advance();
     }
     pin_matrix_step();
     step_end<false>();
