@@ -31,7 +31,7 @@ def draw(case):
     return np.random.default_rng(1_000_003 * case + 17)
 
 
-@pytest.mark.parametrize("case", range(16))
+@pytest.mark.parametrize("case", range(32))
 def test_random_prefill(A, case):
     rng = draw(case)
     hq, hkv = HEADS[rng.integers(len(HEADS))]
@@ -46,7 +46,7 @@ def test_random_prefill(A, case):
     assert_close(out, oracle.attention(f64(q), f64(k), f64(v), w.scale, causal), w.name)
 
 
-@pytest.mark.parametrize("case", range(12))
+@pytest.mark.parametrize("case", range(24))
 def test_random_varlen(A, case):
     rng = draw(100 + case)
     hq, hkv = HEADS[rng.integers(len(HEADS))]
@@ -81,7 +81,7 @@ def random_decode_shape(rng):
     return hq, hkv, d, dtype, batch, max_len, lens, splits
 
 
-@pytest.mark.parametrize("case", range(12))
+@pytest.mark.parametrize("case", range(24))
 def test_random_decode(A, case):
     rng = draw(200 + case)
     hq, hkv, d, dtype, batch, max_len, lens, S = random_decode_shape(rng)
@@ -95,7 +95,7 @@ def test_random_decode(A, case):
     assert_close(out, oracle.decode(f64(q), f64(kc), f64(vc), lens.numpy(), w.scale), w.name)
 
 
-@pytest.mark.parametrize("case", range(8))
+@pytest.mark.parametrize("case", range(16))
 def test_random_paged_decode(A, case):
     rng = draw(300 + case)
     hq, hkv, d, dtype, batch, max_len, lens, S = random_decode_shape(rng)
@@ -116,7 +116,7 @@ def test_random_paged_decode(A, case):
     assert_close(out, ref, w.name)
 
 
-@pytest.mark.parametrize("case", range(6))
+@pytest.mark.parametrize("case", range(12))
 def test_random_q4_decode(A, case):
     rng = draw(400 + case)
     hq, hkv, d, dtype, batch, max_len, lens, S = random_decode_shape(rng)
