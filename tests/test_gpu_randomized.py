@@ -131,3 +131,24 @@ def test_random_q4_decode(A, case):
     ref = oracle.decode_q4(f64(q), kq.cpu().numpy(), ks.cpu().double().numpy(), vq.cpu().numpy(),
                            vs.cpu().double().numpy(), lens.numpy(), w.scale, rotated)
     assert_close(out, ref, w.name)
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_random_prefill_long_sampled(A, case):
+    """Longer random prefill problems (1000..9000 rows, many tiles and stage wrap-arounds, ragged tails);
+    the first, last and random rows of the first and last head against the oracle."""
+    rng = draw(500 + case)
+    hq, hkv = HEADS[rng.integers(len(HEADS))]
+    n, d = int(rng.integers(1000, 9001)), int(rng.choice([64, 128]))
+    causal, dtype = bool(rng.integers(2)), str(rng.choice(["bf16", "f16"]))
+    w = workloads.Prefill(f"random_long_{case}", 1, hq, hkv, n, d, causal, dtype)
+    announce(f"{w.name}: hq={hq} hkv={hkv} n={n} d={d} causal={causal} {dtype}")
+    q, k, v = (t.to(DEV) for t in workloads.prefill_inputs(w))
+    out = A.prefill_fwd(q, k, v, causal=causal, scale=w.scale)
+    torch.cuda.synchronize()
+    g = hq // hkv
+    rows = np.unique(np.concatenate([np.arange(0, 40), np.arange(n - 40, n), rng.integers(0, n, 40)]))
+    for h in sorted({0, hq - 1}):
+        ref = oracle.attention_rows(f64(q[0, h, rows]), f64(k[0, h // g]), f64(v[0, h // g]), w.scale,
+                                    rows if causal else None)
+        assert_close(out[0, h, rows], ref, f"{w.name} h={h}")
