@@ -152,3 +152,28 @@ def test_random_prefill_long_sampled(A, case):
         ref = oracle.attention_rows(f64(q[0, h, rows]), f64(k[0, h // g]), f64(v[0, h // g]), w.scale,
                                     rows if causal else None)
         assert_close(out[0, h, rows], ref, f"{w.name} h={h}")
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_random_decode_long(A, case):
+    """Longer random caches (up to 60000 positions, the split heuristic's and random split counts),
+    contiguous and in pages, against the oracle."""
+    rng = draw(600 + case)
+    hq, hkv = HEADS[rng.integers(len(HEADS))]
+    d, dtype = int(rng.choice([64, 128])), str(rng.choice(["bf16", "f16"]))
+    batch, max_len = int(rng.integers(1, 4)), int(rng.integers(5000, 60001))
+    lens = torch.tensor(rng.integers(max_len // 2, max_len + 1, batch), dtype=torch.int32)
+    S = [None, int(rng.integers(2, 300))][rng.integers(2)]
+    page = int(rng.choice([16, 64, 256]))
+    w = workloads.Decode(f"random_decode_long_{case}", batch, hq, hkv, d, max_len, None, 1.0, dtype)
+    announce(f"{w.name}: B={batch} hq={hq} hkv={hkv} d={d} {dtype} L={max_len} lens={lens.tolist()} S={S} "
+             f"page={page}")
+    q, kc, vc, lens = workloads.decode_inputs(w, device=DEV, kv_lens=lens, max_kv_len=max_len, batch=batch)
+    out = A.decode(q, kc, vc, lens.to(DEV), S, w.scale)
+    torch.cuda.synchronize()
+    ref = oracle.decode(f64(q), f64(kc), f64(vc), lens.numpy(), w.scale)
+    assert_close(out, ref, w.name)
+    kp, vp, table = workloads.paged_from_cache(kc, vc, lens, page, workloads.seed_for(w.name, "pages", 0))
+    outp = A.decode_paged(q, kp, vp, table.to(DEV), lens.to(DEV), S, w.scale)
+    torch.cuda.synchronize()
+    assert_close(outp, ref, w.name + " paged")
