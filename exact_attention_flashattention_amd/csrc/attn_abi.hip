@@ -13,7 +13,7 @@ namespace {
 
 constexpr long long kMaxElems = 1LL << 40;  // per-tensor element bound the kernels' 64-bit offsets assume
 constexpr int kDecodeTargetWaves = 2048;    // decode waves that fill 256 CUs at 8 waves per CU
-constexpr int kDecodeMaxChunk = 1024;       // most keys per split, so ragged lengths balance across waves
+constexpr int kDecodeMaxChunk = 2048;       // most keys per split, so ragged lengths balance across waves
 constexpr int kDecodeMinChunk = 256;        // fewest keys worth a split of its own
 constexpr int kChunkAlign = 64;
 
