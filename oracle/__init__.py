@@ -19,6 +19,7 @@ from .attention import (  # noqa: F401
     decode_paged,
     decode_q4,
     dequantize_e2m1_rows,
+    quantize_e2m1_rows,
     e2m1_value,
     hadamard,
     gather_pages,

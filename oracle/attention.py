@@ -305,6 +305,60 @@ def dequantize_e2m1_rows(codes, scales, rotated: bool):
     return vals
 
 
+def quantize_e2m1_rows(x, rotated: bool):
+    """The 4-bit cache's encoder: rows ``x [..., d]`` (values exact in fp32)
+    -> ``(codes uint8 [..., d/2], scales float32 [...])``, the inverse
+    direction of ``dequantize_e2m1_rows``.
+
+    The pages give no encoder ("Why a quantised cache needs a fused kernel"
+    names 4-bit codes, a per-row norm and an optional Hadamard-rotated domain
+    only), so the procedure is this design's, fixed step by step in fp32 so
+    that any encoder following it writes the same bytes:
+
+    1. with ``rotated``, ``y = R·x`` as Walsh-Hadamard butterflies over the
+       element index bits from bit 0 upward (the lower element ``a`` and the
+       upper ``b`` become ``a + b`` and ``a - b``, each rounded to fp32), then
+       one fp32 multiplication by ``1/sqrt(d)`` rounded to fp32;
+    2. the row scale is ``max|y| / 6`` (fp32 division; 6 is the largest E2M1
+       magnitude), or 1 for an all-zero row;
+    3. each ``t = y / scale`` (fp32 division) takes the code of the E2M1
+       value nearest to it -- found by measuring the distance to all eight
+       magnitudes -- with a tie going to the code whose mantissa bit is clear
+       (round half to even), and the sign bit set when ``t < 0``.
+
+    A row holding NaN gets a NaN scale and code 0 everywhere (no consumer
+    reads such rows: they lie past a sequence's length).
+    """
+    y = np.array(x, dtype=np.float32)
+    d = y.shape[-1]
+    if rotated:
+        h = 1
+        while h < d:
+            blocks = y.reshape(y.shape[:-1] + (d // (2 * h), 2, h))
+            lower, upper = blocks[..., 0, :], blocks[..., 1, :]
+            y = np.stack([lower + upper, lower - upper], axis=-2).reshape(y.shape)
+            h *= 2
+        y = y * np.float32(1.0 / math.sqrt(d))
+    with np.errstate(invalid="ignore"):
+        amax = np.abs(y).max(axis=-1)
+        bad = np.isnan(amax)
+        scale = np.where(amax > 0, amax / np.float32(6.0), np.float32(1.0)).astype(np.float32)
+        scale[bad] = np.nan
+        t = (y / np.where(bad, np.float32(1.0), scale)[..., None]).astype(np.float32)
+    t[np.broadcast_to(bad[..., None], t.shape)] = 0.0
+    # distances (exact in fp64: t and every magnitude are fp32 values) to the
+    # magnitudes of codes 0..7, the code's low bit being its mantissa bit
+    mags = np.abs(e2m1_value(np.arange(8)))
+    dist = np.abs(np.abs(t.astype(np.float64))[..., None] - mags)
+    best = dist.min(axis=-1, keepdims=True)
+    nearest = dist == best
+    even_tie = nearest & (np.arange(8) % 2 == 0)
+    idx = np.where(even_tie.any(axis=-1), even_tie.argmax(axis=-1), nearest.argmax(axis=-1))
+    code = idx.astype(np.uint8) | ((t < 0).astype(np.uint8) << 3)
+    packed = (code[..., 0::2] | (code[..., 1::2] << 4)).astype(np.uint8)
+    return packed, scale
+
+
 def decode_q4(q, k_codes, k_scales, v_codes, v_scales, kv_lens, scale: float, rotated: bool):
     """Single-query attention over a 4-bit cache: the rows are dequantised and
     the plain ``decode`` runs on them ("Why a quantised cache needs a fused

@@ -1,0 +1,39 @@
+"""4-bit cache inputs for the GPU tests, encoded by the oracle's encoder.
+
+The decode workloads' bf16/fp16 caches (from ``workloads``) are encoded on
+the host with ``oracle.quantize_e2m1_rows``, one KV head at a time, and the
+codes and scales are uploaded; the HIP decode and the oracle then read the
+very same cache, none of it produced by the HIP path.
+"""
+
+import numpy as np
+import torch
+
+import oracle
+import workloads
+
+
+def encode(x: torch.Tensor, rotated: bool, device):
+    """``x [..., L, d]`` (any device) -> device tensors ``codes [..., L, d/2]``
+    uint8 and ``scales [..., L]`` fp32, encoded on the host."""
+    lead = x.shape[:-2]
+    flat = x.reshape((-1,) + tuple(x.shape[-2:]))
+    codes = np.empty(flat.shape[:-1] + (x.shape[-1] // 2,), dtype=np.uint8)
+    scales = np.empty(flat.shape[:-1], dtype=np.float32)
+    for i in range(flat.shape[0]):
+        codes[i], scales[i] = oracle.quantize_e2m1_rows(flat[i].float().cpu().numpy(), rotated)
+    return (torch.from_numpy(codes).reshape(lead + codes.shape[1:]).to(device),
+            torch.from_numpy(scales).reshape(lead + scales.shape[1:]).to(device))
+
+
+def q4_inputs(w, rotated: bool, device, salt: int = 0, kv_lens=None, max_kv_len=None, batch=None, v_mult=None):
+    """The decode workload's q and lengths with its NaN-padded caches encoded as
+    4-bit rows: ``(q, k_codes, k_scales, v_codes, v_scales, kv_lens)``.
+    ``v_mult`` scales the V cache before encoding (large-value cases)."""
+    q, kc, vc, lens = workloads.decode_inputs(w, device, salt, kv_lens, max_kv_len, batch)
+    if v_mult is not None:
+        vc = (vc.float() * v_mult).to(vc.dtype)
+    kq, ks = encode(kc, rotated, device)
+    del kc
+    vq, vs = encode(vc, rotated, device)
+    return q, kq, ks, vq, vs, lens

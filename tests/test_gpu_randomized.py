@@ -11,6 +11,7 @@ import pytest
 import torch
 
 import oracle
+import q4cache
 import workloads
 from test_gpu_parity import assert_close, announce, f64
 
@@ -124,8 +125,7 @@ def test_random_q4_decode(A, case):
     w = workloads.Decode(f"random_q4_{case}", batch, hq, hkv, d, max_len, None, 1.0, dtype)
     announce(f"{w.name}: B={batch} hq={hq} hkv={hkv} d={d} {dtype} L={max_len} lens={lens.tolist()} S={S} "
              f"rotated={rotated}")
-    q, kq, ks, vq, vs, lens = workloads.decode_q4_inputs(w, rotated, device=DEV, kv_lens=lens, max_kv_len=max_len,
-                                                         batch=batch)
+    q, kq, ks, vq, vs, lens = q4cache.q4_inputs(w, rotated, DEV, kv_lens=lens, max_kv_len=max_len, batch=batch)
     out = A.decode_q4(q, kq, ks, vq, vs, lens.to(DEV), rotated, S, w.scale)
     torch.cuda.synchronize()
     ref = oracle.decode_q4(f64(q), kq.cpu().numpy(), ks.cpu().double().numpy(), vq.cpu().numpy(),

@@ -597,20 +597,61 @@ def test_dequantize_nibble_order_and_scale():
 
 @pytest.mark.parametrize("rotated", [False, True])
 def test_encoder_decoder_round_trip_within_half_a_step(rotated):
-    """The input encoder and the oracle's decoder agree: each element lands on
-    the nearest E2M1 magnitude, so the error in the stored domain is at most
-    half the gap around it times the scale (the largest half gap is 1, between
-    4 and 6); the rotation preserves the error's norm."""
-    x = torch.randn(64, 128, generator=torch.Generator().manual_seed(3), dtype=torch.float32)
-    codes, scales = workloads.quantize_e2m1_rows(x, rotated)
-    back = oracle.dequantize_e2m1_rows(codes.numpy(), scales.numpy(), rotated)
-    xs = x.double().numpy() @ (oracle.hadamard(128) if rotated else np.eye(128))
+    """The oracle's encoder and decoder agree: each element lands on the
+    nearest E2M1 magnitude, so the error in the stored domain is at most half
+    the gap around it times the scale (the largest half gap is 1, between 4 and
+    6); the rotation preserves the error's norm; each row's largest element is
+    stored as ±6 exactly."""
+    x = torch.randn(64, 128, generator=torch.Generator().manual_seed(3), dtype=torch.float32).numpy()
+    codes, scales = oracle.quantize_e2m1_rows(x, rotated)
+    assert codes.dtype == np.uint8 and codes.shape == (64, 64) and scales.dtype == np.float32
+    back = oracle.dequantize_e2m1_rows(codes, scales, rotated)
+    xs = x.astype(np.float64) @ (oracle.hadamard(128) if rotated else np.eye(128))
     bs = back @ (oracle.hadamard(128) if rotated else np.eye(128))
-    t = np.abs(xs) / scales.double().numpy()[:, None]
+    t = np.abs(xs) / scales.astype(np.float64)[:, None]
     half_gap = np.select([t <= 2, t <= 4], [0.25, 0.5], 1.0)
-    assert np.all(np.abs(bs - xs) <= half_gap * scales.double().numpy()[:, None] * (1 + 1e-6))
-    assert np.allclose(np.linalg.norm(back - x.double().numpy(), axis=1), np.linalg.norm(bs - xs, axis=1))
+    assert np.all(np.abs(bs - xs) <= half_gap * scales.astype(np.float64)[:, None] * (1 + 1e-6))
+    assert np.allclose(np.linalg.norm(back - x.astype(np.float64), axis=1), np.linalg.norm(bs - xs, axis=1))
     assert np.all(np.abs(t).max(axis=1) <= 6 * (1 + 1e-6))
+    assert np.allclose(np.abs(bs).max(axis=1), 6.0 * scales.astype(np.float64), rtol=1e-12, atol=0)
+
+
+def test_encoder_ties_go_to_the_even_code():
+    """A row whose largest magnitude is 6 has scale 1, so its values are
+    encoded as they are.  Every midpoint between neighbouring E2M1 magnitudes
+    goes to the code whose mantissa bit is clear: 0.25 -> 0 (code 0),
+    0.75 -> 1 (2), 1.25 -> 1 (2), 1.75 -> 2 (4), 2.5 -> 2 (4), 3.5 -> 4 (6),
+    5 -> 4 (6), 6 -> 6 (7); bytes pair (low, high) nibbles.  Just off each
+    midpoint the nearer value wins, and negative values set bit 3."""
+    ties = np.array([[0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0]], dtype=np.float32)
+    codes, scales = oracle.quantize_e2m1_rows(ties, False)
+    assert scales.tolist() == [1.0]
+    assert codes.tolist() == [[0x20, 0x42, 0x64, 0x76]]
+    codes, _ = oracle.quantize_e2m1_rows(-ties, False)
+    assert codes.tolist() == [[0xA8, 0xCA, 0xEC, 0xFE]]
+    near = np.array([[0.26, 0.74, 1.26, 1.74, 2.51, 3.49, 5.01, -6.0]], dtype=np.float32)
+    codes, _ = oracle.quantize_e2m1_rows(near, False)
+    assert codes.tolist() == [[0x11, 0x33, 0x55, 0xF7]]
+
+
+def test_encoder_scale_zero_row_and_rotation_by_hand():
+    """Scale = max|y| / 6 in fp32; an all-zero row has scale 1 and code 0
+    everywhere.  Rotated, x = (1, 2, 3, 4) becomes H_4·x / 2 = (5, -1, -2, 0)
+    (butterflies over bit 0: (3, -1, 7, -1); bit 1: (10, -2, -4, 0); times
+    1/2), scale 5/6, t = (6, -1.2, -2.4, 0) -> codes 7, 8|2, 8|4, 0."""
+    codes, scales = oracle.quantize_e2m1_rows(np.zeros((2, 16), dtype=np.float32), True)
+    assert scales.tolist() == [1.0, 1.0] and not codes.any()
+    x = np.array([[1.0, 2.0, 3.0, 4.0]], dtype=np.float32)
+    codes, scales = oracle.quantize_e2m1_rows(x, True)
+    assert scales[0] == np.float32(5.0) / np.float32(6.0)
+    assert codes.tolist() == [[0xA7, 0x0C]]
+    H4 = np.array([[1, 1, 1, 1], [1, -1, 1, -1], [1, 1, -1, -1], [1, -1, -1, 1]]) / 2.0
+    assert np.array_equal(H4 @ x[0].astype(np.float64), [5.0, -1.0, -2.0, 0.0])
+    codes, scales = oracle.quantize_e2m1_rows(np.array([[3.0, -12.0, 1.0, 0.0]], dtype=np.float32), False)
+    assert scales.tolist() == [2.0] and codes.tolist() == [[0xF3, 0x01]]  # t = (1.5, -6, 0.5, 0)
+    nan_row = np.array([[1.0, np.nan, 2.0, 3.0]], dtype=np.float32)
+    codes, scales = oracle.quantize_e2m1_rows(nan_row, False)
+    assert np.isnan(scales[0]) and not codes.any()
 
 
 def test_decode_q4_is_decode_on_dequantised_rows_and_single_key_exact():

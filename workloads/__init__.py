@@ -271,64 +271,6 @@ def paged_from_cache(k_cache: torch.Tensor, v_cache: torch.Tensor, kv_lens: torc
     return pools[0], pools[1], table
 
 
-# ---- 4-bit cache encoding (input preparation for the fused-dequant decode) ----------------
-#
-# Rows of d values are stored as OCP MX E2M1 codes (4 bits: sign, 2 exponent bits with bias 1, 1 mantissa
-# bit; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) with one fp32 scale per row, optionally after the rotation
-# R = H_d / sqrt(d) (normalised Sylvester-Hadamard).  Byte i of a row holds element 2i in its low nibble and
-# element 2i+1 in its high nibble.  This is the encoder only; decoding is the consumer's business.
-
-_E2M1_MAGNITUDES = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
-
-
-def quantize_e2m1_rows(x: torch.Tensor, rotated: bool):
-    """Encode rows ``x [..., d]`` as ``(codes uint8 [..., d/2], scales float32 [...])``.
-
-    The row (rotated by R first if ``rotated``: fp32 butterflies over the
-    index bits from bit 0 upward, then a multiplication by fp32(1/sqrt(d))) is
-    divided by its scale
-    ``max|row| / 6`` (1 for an all-zero row) and every element takes the code
-    of the nearest E2M1 magnitude (ties to the even code), with the sign bit
-    set for negative values.  Rows holding NaN keep a NaN scale.
-    """
-    d = x.shape[-1]
-    y = x.float()
-    if rotated:
-        # R·x as fp32 butterflies over the index bits from bit 0 upward, then one
-        # multiplication by 1/sqrt(d) rounded to fp32 (a fixed procedure, so that
-        # every encoder following it produces the same codes)
-        h = 1
-        while h < d:
-            v = y.reshape(*y.shape[:-1], d // (2 * h), 2, h)
-            y = torch.stack([v[..., 0, :] + v[..., 1, :], v[..., 0, :] - v[..., 1, :]], dim=-2).reshape(y.shape)
-            h *= 2
-        y = y * torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32)
-    amax = y.abs().amax(dim=-1)
-    scale = torch.where(amax > 0, amax / 6.0, torch.ones_like(amax))
-    scale = torch.where(torch.isnan(amax), amax, scale).to(torch.float32)
-    t = (y / scale.unsqueeze(-1)).nan_to_num(0.0)
-    mags = _E2M1_MAGNITUDES.to(device=x.device)
-    dist = (t.abs().unsqueeze(-1) - mags).abs()
-    # nearest magnitude; on a tie the even index (its mantissa bit clear) wins
-    best = dist.min(dim=-1, keepdim=True).values
-    cand = (dist <= best) & (torch.arange(8, device=x.device) % 2 == 0)
-    idx = torch.where(cand.any(-1), cand.float().argmax(-1), dist.argmin(-1))
-    code = idx.to(torch.uint8) | ((t < 0).to(torch.uint8) << 3)
-    packed = code[..., 0::2] | (code[..., 1::2] << 4)
-    return packed.contiguous(), scale.contiguous()
-
-
-def decode_q4_inputs(w: Decode, rotated: bool, device="cpu", salt: int = 0, kv_lens: Optional[torch.Tensor] = None,
-                     max_kv_len: Optional[int] = None, batch: Optional[int] = None):
-    """The decode workload's q and lengths with its NaN-padded caches encoded
-    as 4-bit rows: ``(q, k_codes, k_scales, v_codes, v_scales, kv_lens)``."""
-    q, kc, vc, lens = decode_inputs(w, device, salt, kv_lens, max_kv_len, batch)
-    kq, ks = quantize_e2m1_rows(kc, rotated)
-    del kc
-    vq, vs = quantize_e2m1_rows(vc, rotated)
-    return q, kq, ks, vq, vs, lens
-
-
 def pages_decode_kv_bytes(seq_len: int, batch: int, kv_heads: int, head_dim: int, layers: int,
                           bytes_per_value: int = 2) -> float:
     """KV bytes one decode step reads for a whole model: K and V, every layer,
