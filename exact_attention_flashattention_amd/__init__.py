@@ -63,6 +63,39 @@ def _scale(scale: Optional[float], d: int) -> float:
     return float(1.0 / math.sqrt(d)) if scale is None else float(scale)
 
 
+def _check(t: torch.Tensor, name: str, shape, dtype: torch.dtype, device: torch.device) -> torch.Tensor:
+    """A caller-supplied buffer must be exactly what the kernels will write:
+    the kernels trust the sizes they are given, so a wrong one is refused here."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    return t
+
+
+def _same_device(ref: torch.Tensor, **tensors) -> None:
+    for name, t in tensors.items():
+        if t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, expected {ref.device}")
+
+
+def _partials(partials, B: int, hq: int, S: int, d: int, device: torch.device):
+    """The split-K workspace ``(m [B, hq, S], l [B, hq, S], o [B, hq, S, d])``, fp32 on ``device``:
+    allocated here when not given, else checked against the split count the call uses."""
+    if partials is None:
+        return (torch.empty((B, hq, S), dtype=torch.float32, device=device),
+                torch.empty((B, hq, S), dtype=torch.float32, device=device),
+                torch.empty((B, hq, S, d), dtype=torch.float32, device=device))
+    if len(partials) != 3:
+        raise ValueError("partials must be a (part_m, part_l, part_o) triple")
+    pm, pl, po = partials
+    return (_check(pm, "part_m", (B, hq, S), torch.float32, device),
+            _check(pl, "part_l", (B, hq, S), torch.float32, device),
+            _check(po, "part_o", (B, hq, S, d), torch.float32, device))
+
+
 def prefill_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
                 scale: Optional[float] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Exact attention of ``q: [B, Hq, N, d]`` over ``k, v: [B, Hkv, N, d]``; returns ``[B, Hq, N, d]``."""
@@ -72,8 +105,8 @@ def prefill_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool 
     B, hq, n, d = q.shape
     if k.shape[0] != B or k.shape[2] != n or k.shape[3] != d or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v disagree in batch, length, head dim or dtype")
-    if out is None:
-        out = torch.empty_like(q)
+    _same_device(q, k=k, v=v)
+    out = torch.empty_like(q) if out is None else _check(out, "out", q.shape, q.dtype, q.device)
     st = lib.attn_prefill_fwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), _dtype_code(q), B, hq,
                               k.shape[1], n, d, _scale(scale, d), int(bool(causal)), _stream(q))
     _lib.check("attn_prefill_fwd", st)
@@ -104,8 +137,8 @@ def prefill_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seq
     if alibi_slopes is not None and (alibi_slopes.dtype != torch.float32 or alibi_slopes.numel() != hq
                                      or alibi_slopes.device != q.device):
         raise ValueError("alibi_slopes must be a float32 device tensor with one slope per query head")
-    if out is None:
-        out = torch.empty_like(q)
+    _same_device(q, k=k, v=v)
+    out = torch.empty_like(q) if out is None else _check(out, "out", q.shape, q.dtype, q.device)
     st = lib.attn_prefill_varlen_fwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
                                      _dev(cu_seqlens_q, "cu_seqlens_q"), _dev(cu_seqlens_k, "cu_seqlens_k"), total_q,
                                      total_k, int(max_seqlen_q), int(max_seqlen_k), _dtype_code(q),
@@ -140,13 +173,9 @@ def decode_splitk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         raise ValueError("q and caches disagree in batch, head dim or dtype")
     if kv_lens.dtype != torch.int32 or kv_lens.numel() != B or kv_lens.device != q.device:
         raise ValueError("kv_lens must be an int32 device tensor with one entry per sequence")
+    _same_device(q, k_cache=k_cache, v_cache=v_cache)
     S = decode_num_splits(B, hkv, L) if num_splits is None else int(num_splits)
-    if partials is None:
-        pm = torch.empty((B, hq, S), dtype=torch.float32, device=q.device)
-        pl = torch.empty((B, hq, S), dtype=torch.float32, device=q.device)
-        po = torch.empty((B, hq, S, d), dtype=torch.float32, device=q.device)
-    else:
-        pm, pl, po = partials
+    pm, pl, po = _partials(partials, B, hq, S, d, q.device)
     st = lib.attn_decode_splitk(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
                                 _dev(kv_lens, "kv_lens"), L, _dtype_code(q), B, hq, hkv, d, _scale(scale, d), S,
                                 _dev(pm, "part_m"), _dev(pl, "part_l"), _dev(po, "part_o"), _stream(q))
@@ -174,14 +203,10 @@ def decode_splitk_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.T
     if alibi_slopes is not None and (alibi_slopes.dtype != torch.float32 or alibi_slopes.numel() != hq
                                      or alibi_slopes.device != q.device):
         raise ValueError("alibi_slopes must be a float32 device tensor with one slope per query head")
+    _same_device(q, k_pages=k_pages, v_pages=v_pages)
     max_pages = block_table.shape[1]
     S = decode_num_splits(B, hkv, max_pages * page) if num_splits is None else int(num_splits)
-    if partials is None:
-        pm = torch.empty((B, hq, S), dtype=torch.float32, device=q.device)
-        pl = torch.empty((B, hq, S), dtype=torch.float32, device=q.device)
-        po = torch.empty((B, hq, S, d), dtype=torch.float32, device=q.device)
-    else:
-        pm, pl, po = partials
+    pm, pl, po = _partials(partials, B, hq, S, d, q.device)
     st = lib.attn_decode_splitk_paged(_dev(q, "q"), _dev(k_pages, "k_pages"), _dev(v_pages, "v_pages"),
                                       _dev(block_table, "block_table"), max_pages, P, page,
                                       _dev(kv_lens, "kv_lens"), _dtype_code(q), B, hq, hkv, d, _scale(scale, d), S,
@@ -208,13 +233,9 @@ def decode_splitk_q4(q: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Ten
             raise ValueError(f"{name} must be float32 [B, Hkv, Lmax]")
     if kv_lens.dtype != torch.int32 or kv_lens.numel() != B or kv_lens.device != q.device:
         raise ValueError("kv_lens must be an int32 device tensor with one entry per sequence")
+    _same_device(q, k_codes=k_codes, v_codes=v_codes, k_scales=k_scales, v_scales=v_scales)
     S = decode_num_splits(B, hkv, L) if num_splits is None else int(num_splits)
-    if partials is None:
-        pm = torch.empty((B, hq, S), dtype=torch.float32, device=q.device)
-        pl = torch.empty((B, hq, S), dtype=torch.float32, device=q.device)
-        po = torch.empty((B, hq, S, d), dtype=torch.float32, device=q.device)
-    else:
-        pm, pl, po = partials
+    pm, pl, po = _partials(partials, B, hq, S, d, q.device)
     st = lib.attn_decode_splitk_q4(_dev(q, "q"), _dev(k_codes, "k_codes"), _dev(k_scales, "k_scales"),
                                    _dev(v_codes, "v_codes"), _dev(v_scales, "v_scales"), _dev(kv_lens, "kv_lens"), L,
                                    _dtype_code(q), B, hq, hkv, d, _scale(scale, d), int(bool(rotated)), S,
@@ -231,19 +252,23 @@ def kv_quantize_q4(x: torch.Tensor, rotated: bool, out_rows: Optional[torch.Tens
     lib = _lib_handle()
     d = x.shape[-1]
     rows = x.numel() // d
+    if (codes is None) != (scales is None):
+        raise ValueError("give both codes and scales, or neither")
     if out_rows is None:
         if codes is None:
             codes = torch.empty(x.shape[:-1] + (d // 2,), dtype=torch.uint8, device=x.device)
             scales = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+        _check(codes, "codes", x.shape[:-1] + (d // 2,), torch.uint8, x.device)
+        _check(scales, "scales", x.shape[:-1], torch.float32, x.device)
         capacity = rows
     else:
-        if codes is None or scales is None:
+        if codes is None:
             raise ValueError("out_rows needs the destination codes and scales")
         if out_rows.dtype != torch.int32 or out_rows.numel() != rows or out_rows.device != x.device:
             raise ValueError("out_rows must be an int32 device tensor with one entry per row")
         capacity = scales.numel()
-    if codes.dtype != torch.uint8 or scales.dtype != torch.float32 or codes.numel() != scales.numel() * (d // 2):
-        raise ValueError("codes must be uint8 [capacity, d/2] and scales float32 [capacity]")
+        _check(codes, "codes", (capacity, d // 2), torch.uint8, x.device)
+        _check(scales, "scales", (capacity,), torch.float32, x.device)
     st = lib.attn_kv_quantize_q4(_dev(x, "x"), rows, d, _dtype_code(x), int(bool(rotated)),
                                  None if out_rows is None else _dev(out_rows, "out_rows"), capacity,
                                  _dev(codes, "codes"), _dev(scales, "scales"), _stream(x))
@@ -255,13 +280,20 @@ def merge_partials(part_m: torch.Tensor, part_l: torch.Tensor, part_o: torch.Ten
                    out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Merge ``[B, Hq, S]`` / ``[B, Hq, S, d]`` fp32 partials into ``[B, Hq, d]`` of ``out_dtype``."""
     lib = _lib_handle()
+    if part_o.dim() != 4:
+        raise ValueError("part_o must be [B, Hq, S, d]")
     B, hq, S, d = part_o.shape
     if part_m.shape != (B, hq, S) or part_l.shape != (B, hq, S):
         raise ValueError("partial shapes disagree")
     if any(t.dtype != torch.float32 for t in (part_m, part_l, part_o)):
         raise TypeError("partials must be float32")
+    _same_device(part_o, part_m=part_m, part_l=part_l)
     if out is None:
         out = torch.empty((B, hq, d), dtype=out_dtype, device=part_o.device)
+    elif out.dtype not in _DTYPES:
+        raise ValueError(f"out must be bfloat16 or float16, got {out.dtype}")
+    else:
+        _check(out, "out", (B, hq, d), out.dtype, part_o.device)
     st = lib.attn_merge_partials(_dev(part_m, "part_m"), _dev(part_l, "part_l"), _dev(part_o, "part_o"), B, hq, d,
                                  S, _dev(out, "out"), _DTYPES[out.dtype], _stream(part_o))
     _lib.check("attn_merge_partials", st)

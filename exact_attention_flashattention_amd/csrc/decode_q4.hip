@@ -29,6 +29,12 @@
 // consecutive dimensions (16 at d=64) and reads its K codes with one 16-byte
 // (8-byte) load.  V is dequantised into wave-private LDS in natural order and
 // read back with the transpose read as in the 16-bit kernel.
+//
+// The P·V product runs in bf16 whatever the query's type: its B operand is a
+// probability (up to 2^8 before the reference is raised) times the V row's
+// scale, which for legal fp16 V rows (|v| up to 65504, scale up to ~1.1e4)
+// would overflow fp16; E2M1 values are exact in bf16, and bf16 has fp32's
+// range.
 #include "device_common.hpp"
 #include "launchers.hpp"
 
@@ -264,11 +270,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
     for (int i = 0; i < VB / 16; ++i) {
       u32x4 lo, hi;
-      dequant8<T>(u32x2{st.v[i][0], st.v[i][1]}, lo, hi);
+      dequant8<Bf16>(u32x2{st.v[i][0], st.v[i][1]}, lo, hi);
       const uint32_t at = vrow * VP + (lane & 1) * D + i * 64;
       lds_write16(vlds, at, lo);
       lds_write16(vlds, at + 16, hi);
-      dequant8<T>(u32x2{st.v[i][2], st.v[i][3]}, lo, hi);
+      dequant8<Bf16>(u32x2{st.v[i][2], st.v[i][3]}, lo, hi);
       lds_write16(vlds, at + 32, lo);
       lds_write16(vlds, at + 48, hi);
     }
@@ -325,8 +331,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         s[sb][e] = p * st.vs[sb][e];  // the V row's scale rides on its probability
       }
     l_run += psum;
-    const u32x4 pf = {T::pack2(s[0][0], s[0][1]), T::pack2(s[0][2], s[0][3]), T::pack2(s[1][0], s[1][1]),
-                      T::pack2(s[1][2], s[1][3])};
+    const u32x4 pf = {Bf16::pack2(s[0][0], s[0][1]), Bf16::pack2(s[0][2], s[0][3]), Bf16::pack2(s[1][0], s[1][1]),
+                      Bf16::pack2(s[1][2], s[1][3])};
     __syncthreads();  // V rows are in LDS
     const uint32_t row_a = (4 * grp + (r >> 2)) * VP;
     const uint32_t row_b = (16 + 4 * grp + (r >> 2)) * VP;
@@ -335,7 +341,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       const uint32_t col = (dt * 16 + 4 * (r & 3)) * 2;
       const u32x2 va = lds_read_tr16(vlds, row_a + col);
       const u32x2 vb = lds_read_tr16(vlds, row_b + col);
-      oacc[dt] = T::mfma16(u32x4{va[0], va[1], vb[0], vb[1]}, pf, oacc[dt]);
+      oacc[dt] = Bf16::mfma16(u32x4{va[0], va[1], vb[0], vb[1]}, pf, oacc[dt]);
     }
   };
 
