@@ -7,8 +7,10 @@ to tighter bounds derived from fp32 arithmetic, stated at each check.
 
 Cases run at sizes the oracle finishes in seconds that still span several tiles
 and a ragged tail, plus every benchmarked workload at full size in the launch
-configuration the bench uses, checked on sampled rows (computed one by one by
-the oracle) and on properties that hold at any size.
+configuration the bench uses: whole outputs for the N=4096 prefill batches, the
+262144-position decode (plain, paged and 4-bit) and the 64-sequence ragged
+decode; the causal N=32768 prefill on a row sample over all 32 heads (computed
+row by row by the oracle), and properties that hold at any size.
 """
 
 import math
@@ -18,6 +20,7 @@ import pytest
 import torch
 
 import oracle
+import q4cache
 import workloads
 
 pytestmark = pytest.mark.gpu
@@ -134,10 +137,10 @@ def test_prefill_all_scores_far_below_zero(A, d, causal):
     run_prefill_tensors(A, q.to(DEV), k.to(DEV), v.to(DEV), causal, w.scale, w.name)
 
 
-@pytest.mark.parametrize("name", ["prefill_b4_h32_n4096_d64_bf16", "prefill_b4_h32_n4096_d128_bf16",
-                                  "prefill_causal_gqa_b1_hq32_hkv8_n32768_d128_bf16"])
-def test_prefill_full_size_sampled_rows(A, name):
-    """Full-size workloads in the benchmarked launch; sampled rows vs the oracle."""
+@pytest.mark.parametrize("name", ["prefill_b4_h32_n4096_d64_bf16", "prefill_b4_h32_n4096_d128_bf16"])
+def test_prefill_n4096_whole_output(A, name):
+    """The non-causal batch-4, 32-head, N=4096 workloads at full size in the benchmarked launch: every
+    element of all 128 (batch, head) slices against the oracle; two launches give identical bits."""
     w = workloads.WORKLOADS[name]
     announce(w.name)
     q, k, v = workloads.prefill_inputs(w, device=DEV)
@@ -145,17 +148,43 @@ def test_prefill_full_size_sampled_rows(A, name):
     out2 = A.prefill_fwd(q, k, v, causal=w.causal, scale=w.scale)
     torch.cuda.synchronize()
     assert torch.equal(out, out2), "prefill is not deterministic"
+    ref = oracle.attention(f64(q), f64(k), f64(v), w.scale, w.causal)
+    assert_close(out, ref, f"{w.name} (whole output)")
+
+
+def c3_sample_rows(n, rng):
+    """The routine row sample of the causal N=32768 workload: every row of the first and last 256-row
+    blocks, every row i with i mod 128 in {0, 127} (the first and last row of each 128-row block, where
+    the diagonal and the tile edges meet), and 256 random rows."""
+    return np.unique(np.concatenate([np.arange(0, 256), np.arange(n - 256, n), np.arange(0, n, 128),
+                                     np.arange(127, n, 128), rng.integers(0, n, 256)]))
+
+
+def test_prefill_causal_gqa_32k_all_heads_row_sample(A):
+    """The causal GQA N=32768 workload (32 query heads on 8 KV heads, d=128) in the benchmarked launch:
+    the row sample above, for every one of the 32 query heads, against the oracle computed row by row."""
+    w = workloads.WORKLOADS["prefill_causal_gqa_b1_hq32_hkv8_n32768_d128_bf16"]
+    announce(w.name)
+    q, k, v = workloads.prefill_inputs(w, device=DEV)
+    out = A.prefill_fwd(q, k, v, causal=True, scale=w.scale)
+    out2 = A.prefill_fwd(q, k, v, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2), "prefill is not deterministic"
     assert not torch.isnan(out).any()
     rng = np.random.default_rng(7)
     g = w.hq // w.hkv
-    heads = sorted({0, w.hq - 1, *rng.integers(0, w.hq, 2).tolist()})
-    for b in sorted({0, w.batch - 1}):
-        for h in heads:
-            rows = np.unique(np.concatenate([np.arange(0, 130), np.arange(w.n - 130, w.n),
-                                             np.arange(127, w.n, 1024), rng.integers(0, w.n, 64)]))
-            K, V = f64(k[b, h // g]), f64(v[b, h // g])
-            ref = oracle.attention_rows(f64(q[b, h, rows]), K, V, w.scale, rows if w.causal else None)
-            assert_close(out[b, h, rows], ref, f"{w.name} b={b} h={h}")
+    got, ref = [], []
+    for h in range(w.hq):
+        rows = c3_sample_rows(w.n, rng)
+        if h % g == 0:
+            K, V = f64(k[0, h // g]), f64(v[0, h // g])
+        qh, oh = f64(q[0, h]), f64(out[0, h])
+        for r0 in range(0, len(rows), 256):
+            rr = rows[r0:r0 + 256]
+            ref.append(oracle.attention_rows(qh[rr], K[:rr[-1] + 1], V[:rr[-1] + 1], w.scale, rr))
+            got.append(oh[rr])
+        print(f"head {h}: {len(rows)} rows", flush=True)
+    assert_close(np.concatenate(got), np.concatenate(ref), f"{w.name} (all heads, row sample)")
 
 
 # --- varlen / append prefill ------------------------------------------------------------
@@ -416,25 +445,29 @@ def test_decode_long_context_full(A):
     assert_close(out, ref, DEC.name)
 
 
-def test_decode_ragged_full_sampled(A):
-    """64 ragged sequences (lengths 1024..32768, q x8): the benchmarked launch;
-    8 sequences (shortest, longest and 6 random) checked whole against the oracle."""
+def test_decode_ragged_whole_output(A):
+    """64 ragged sequences (lengths 1024..32768, q x8): the benchmarked launch, every sequence and head
+    against the oracle (rows past each length are NaN in the cache and must never be read)."""
     announce(RAG.name)
     q, kc, vc, lens = workloads.decode_inputs(RAG, device=DEV)
     out = A.decode(q, kc, vc, lens.to(DEV), None, RAG.scale)
+    out2 = A.decode(q, kc, vc, lens.to(DEV), None, RAG.scale)
     torch.cuda.synchronize()
-    assert not torch.isnan(out).any()
+    assert torch.equal(out, out2), "decode is not deterministic"
     g = RAG.hq // RAG.hkv
-    rng = np.random.default_rng(3)
     Ls = lens.numpy()
-    seqs = sorted({int(Ls.argmin()), int(Ls.argmax()), *rng.integers(0, RAG.batch, 6).tolist()})
-    for b in seqs:
+    qf = f64(q)
+    ref = np.zeros((RAG.batch, RAG.hq, RAG.d))
+    for b in range(RAG.batch):
         L = int(Ls[b])
-        ref = np.zeros((RAG.hq, RAG.d))
+        Kb, Vb = f64(kc[b, :, :L]), f64(vc[b, :, :L])
         for kh in range(RAG.hkv):
-            K, V = f64(kc[b, kh, :L]), f64(vc[b, kh, :L])
-            ref[kh * g:(kh + 1) * g] = oracle.attention_rows(f64(q[b, kh * g:(kh + 1) * g]), K, V, RAG.scale)
-        assert_close(out[b], ref, f"{RAG.name} b={b} L={L}")
+            ref[b, kh * g:(kh + 1) * g] = oracle.attention_rows(qf[b, kh * g:(kh + 1) * g], Kb[kh], Vb[kh],
+                                                                RAG.scale)
+        if b % 16 == 15:
+            print(f"sequences 0..{b} done", flush=True)
+    print(f"sum of lengths {int(Ls.sum())}", flush=True)
+    assert_close(out, ref, f"{RAG.name} (whole output)")
 
 
 # --- paged decode ----------------------------------------------------------------------
@@ -572,16 +605,19 @@ def test_decode_paged_long_context_full(A):
 
 # --- 4-bit cache, fused dequant ---------------------------------------------------------
 
-def q4_case(A, w, kv_lens, max_len, batch, num_splits, rotated, seed=0):
+def q4_case(A, w, kv_lens, max_len, batch, num_splits, rotated, seed=0, v_mult=None):
     announce(f"q4 {w.name} B={batch} L={max_len} lens={kv_lens.tolist()[:6]} S={num_splits} rotated={rotated}")
-    q, kq, ks, vq, vs, lens = workloads.decode_q4_inputs(w, rotated, device=DEV, salt=seed, kv_lens=kv_lens,
-                                                         max_kv_len=max_len, batch=batch)
+    q, kq, ks, vq, vs, lens = q4cache.q4_inputs(w, rotated, DEV, salt=seed, kv_lens=kv_lens, max_kv_len=max_len,
+                                                batch=batch, v_mult=v_mult)
     S = A.decode_num_splits(batch, w.hkv, max_len) if num_splits is None else num_splits
     out = A.decode_q4(q, kq, ks, vq, vs, lens.to(DEV), rotated, S, w.scale)
     torch.cuda.synchronize()
     ref = oracle.decode_q4(f64(q), kq.cpu().numpy(), ks.cpu().double().numpy(), vq.cpu().numpy(),
                            vs.cpu().double().numpy(), lens.numpy(), w.scale, rotated)
-    assert_close(out, ref, f"q4 {w.name} S={S} rotated={rotated}")
+    if v_mult is None:
+        assert_close(out, ref, f"q4 {w.name} S={S} rotated={rotated}")
+    else:  # the tolerance is stated for unit-scale values: compare in units of the V scaling
+        assert_close(f64(out) / v_mult, ref / v_mult, f"q4 {w.name} S={S} rotated={rotated} V x{v_mult:g}")
     return out
 
 
@@ -607,11 +643,29 @@ def test_decode_q4_ragged_high_scores(A):
     q4_case(A, RAG, torch.tensor([1024, 3000, 1500, 4096], dtype=torch.int32), 4096, 4, None, True)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("rotated", [False, True])
+def test_decode_q4_fp16_large_values(A, d, rotated):
+    """fp16 queries and caches whose V rows reach about 1e4 in magnitude (legal fp16 values; a row's scale is
+    then ~2e3): the probabilities times the V row scales exceed the fp16 range, so the kernel must not form
+    them in fp16.  Reduced lengths around the split size."""
+    w = workloads.Decode(f"decode_q4_fp16_large_{d}", 3, 16, 2, d, 1024, None, 1.0, "f16")
+    q4_case(A, w, torch.tensor([1024, 700, 65], dtype=torch.int32), 1024, 3, None, rotated, v_mult=8192.0)
+
+
 def test_decode_q4_long_context_full(A):
-    """The 262144-key cache encoded as rotated 4-bit rows, the benchmarked launch,
-    whole output against the oracle on the dequantised rows."""
+    """The 262144-key cache encoded as rotated 4-bit rows (by the oracle's encoder on the host), the
+    benchmarked launch, whole output against the oracle on the dequantised rows; the HIP encoder produces
+    the same codes and scales from the same rows bit for bit."""
     announce(f"q4 {DEC.name}")
-    q, kq, ks, vq, vs, lens = workloads.decode_q4_inputs(DEC, True, device=DEV)
+    q, kc, vc, lens = workloads.decode_inputs(DEC, device=DEV)
+    kq, ks = q4cache.encode(kc, True, DEV)
+    vq, vs = q4cache.encode(vc, True, DEV)
+    hk, hks = A.kv_quantize_q4(kc, True)
+    hv, hvs = A.kv_quantize_q4(vc, True)
+    torch.cuda.synchronize()
+    assert torch.equal(hk, kq) and torch.equal(hks, ks) and torch.equal(hv, vq) and torch.equal(hvs, vs)
+    del kc, vc, hk, hks, hv, hvs
     out = A.decode_q4(q, kq, ks, vq, vs, lens.to(DEV), True, None, DEC.scale)
     torch.cuda.synchronize()
     g = DEC.hq // DEC.hkv
@@ -626,19 +680,21 @@ def test_decode_q4_long_context_full(A):
 
 @pytest.mark.parametrize("d,dtype", [(128, "bf16"), (64, "bf16"), (128, "f16"), (64, "f16")])
 @pytest.mark.parametrize("rotated", [False, True])
-def test_kv_quantize_q4_matches_the_host_encoder_bit_exact(A, d, dtype, rotated):
-    """The HIP encoder and the independent host encoder follow the same fixed
-    fp32 procedure, so codes and scales agree bit for bit; rows include an
-    all-zero row (scale 1) and exact code-boundary values."""
+def test_kv_quantize_q4_matches_the_oracle_encoder_bit_exact(A, d, dtype, rotated):
+    """The HIP encoder and the oracle's encoder follow the same fixed fp32
+    procedure, so codes and scales agree bit for bit; rows include an
+    all-zero row (scale 1) and exact code-boundary values (every midpoint
+    between E2M1 magnitudes, in a row whose scale is exactly 1)."""
     announce(f"quantize d={d} {dtype} rotated={rotated}")
     x = workloads.normal((37, 5, d), dtype, workloads.seed_for("quantize", "x", d), DEV) * 3
     x[0, 0] = 0
     x[1, 1, :8] = torch.tensor([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0], dtype=x.dtype)
+    x[2, 2] = torch.tensor([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0] * (d // 8), dtype=x.dtype)
     codes, scales = A.kv_quantize_q4(x, rotated)
     torch.cuda.synchronize()
-    ref_c, ref_s = workloads.quantize_e2m1_rows(x.cpu(), rotated)
-    assert torch.equal(scales.cpu(), ref_s)
-    assert torch.equal(codes.cpu(), ref_c)
+    ref_c, ref_s = oracle.quantize_e2m1_rows(x.float().cpu().numpy(), rotated)
+    assert np.array_equal(scales.cpu().numpy(), ref_s)
+    assert np.array_equal(codes.cpu().numpy(), ref_c)
     assert scales[0, 0].item() == 1.0 and not codes[0, 0].any()
 
 
@@ -656,11 +712,11 @@ def test_kv_quantize_q4_scatters_rows_and_skips_outside(A):
     scales = torch.full((B * hkv * L,), -1.0, dtype=torch.float32, device=DEV)
     A.kv_quantize_q4(x, True, dst.reshape(-1).to(DEV), codes, scales)
     torch.cuda.synchronize()
-    ref_c, ref_s = workloads.quantize_e2m1_rows(x.cpu().reshape(-1, d), True)
+    ref_c, ref_s = oracle.quantize_e2m1_rows(x.float().cpu().reshape(-1, d).numpy(), True)
     written = torch.zeros(B * hkv * L, dtype=torch.bool)
     for i, r in enumerate(dst.reshape(-1).tolist()):
         if r < B * hkv * L:
-            assert torch.equal(codes[r].cpu(), ref_c[i]) and scales[r].item() == ref_s[i].item()
+            assert np.array_equal(codes[r].cpu().numpy(), ref_c[i]) and scales[r].item() == float(ref_s[i])
             written[r] = True
     assert int(written.sum()) == B * hkv - 1
     assert (codes.cpu()[~written] == 0xAB).all() and (scales.cpu()[~written] == -1.0).all()
@@ -678,8 +734,13 @@ def test_kv_quantize_then_fused_decode(A):
     vq, vs = A.kv_quantize_q4(vc, True)
     out = A.decode_q4(q, kq, ks, vq, vs, lens.to(DEV), True, None, w.scale)
     torch.cuda.synchronize()
-    ref = oracle.decode_q4(f64(q), kq.cpu().numpy(), ks.cpu().double().numpy(), vq.cpu().numpy(),
-                           vs.cpu().double().numpy(), lens.numpy(), w.scale, True)
+    # the oracle reads its own encoding of the same rows, which the HIP encoder's must equal
+    okq, oks = q4cache.encode(kc, True, "cpu")
+    ovq, ovs = q4cache.encode(vc, True, "cpu")
+    assert torch.equal(kq.cpu(), okq) and torch.equal(ks.cpu(), oks)
+    assert torch.equal(vq.cpu(), ovq) and torch.equal(vs.cpu(), ovs)
+    ref = oracle.decode_q4(f64(q), okq.numpy(), oks.double().numpy(), ovq.numpy(), ovs.double().numpy(),
+                           lens.numpy(), w.scale, True)
     assert_close(out, ref, "quantize + q4 decode")
 
 
