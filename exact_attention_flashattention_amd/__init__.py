@@ -18,6 +18,8 @@ Entry points (same names as the C ABI):
 * ``kv_quantize_q4(x, rotated, out_rows, codes, scales)`` -- ``attn_kv_quantize_q4``
 * ``merge_partials(part_m, part_l, part_o, out_dtype)`` -- ``attn_merge_partials``
 * ``decode(...)``, ``decode_paged(...)``, ``decode_q4(...)`` -- split-K then merge, back to back on one stream
+* ``decode_noalloc(q, k_cache, v_cache, kv_lens, num_splits, scale)`` -- ``attn_decode_noalloc``: the same
+  split-K and merge with the partial states in the library's fixed scratch array (no workspace)
 * ``decode_num_splits``, ``decode_chunk_len``, ``decode_workspace_bytes`` -- host helpers
 """
 
@@ -31,7 +33,8 @@ import torch
 from . import _lib
 from ._lib import ATTN_BF16, ATTN_F16, AttnError  # noqa: F401
 
-__all__ = ["prefill_fwd", "prefill_varlen_fwd", "decode_splitk", "decode_splitk_paged", "decode_splitk_q4", "decode_q4", "kv_quantize_q4", "merge_partials", "decode", "decode_paged",
+__all__ = ["prefill_fwd", "prefill_varlen_fwd", "decode_splitk", "decode_splitk_paged", "decode_splitk_q4", "decode_q4",
+           "kv_quantize_q4", "merge_partials", "decode", "decode_paged", "decode_noalloc",
            "decode_num_splits", "decode_chunk_len", "decode_workspace_bytes", "AttnError"]
 
 _DTYPES = {torch.bfloat16: ATTN_BF16, torch.float16: ATTN_F16}
@@ -305,6 +308,30 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_len
     """Single-query decode: split-K partials then their merge, on the current stream."""
     pm, pl, po = decode_splitk(q, k_cache, v_cache, kv_lens, num_splits, scale, partials)
     return merge_partials(pm, pl, po, q.dtype)
+
+
+def decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_lens: torch.Tensor,
+                   num_splits: Optional[int] = None, scale: Optional[float] = None,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Single-query decode in one library call that allocates nothing: the split-K partial states live in
+    the library's fixed per-GPU scratch array.  ``num_splits=None`` lets the library plan the split count.
+    Calls that overlap on one GPU race on that array."""
+    lib = _lib_handle()
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("expected q [B, Hq, d] and caches [B, Hkv, Lmax, d]")
+    B, hq, d = q.shape
+    _, hkv, L, dk = k_cache.shape
+    if k_cache.shape[0] != B or dk != d or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q and caches disagree in batch, head dim or dtype")
+    if kv_lens.dtype != torch.int32 or kv_lens.numel() != B or kv_lens.device != q.device:
+        raise ValueError("kv_lens must be an int32 device tensor with one entry per sequence")
+    _same_device(q, k_cache=k_cache, v_cache=v_cache)
+    out = torch.empty_like(q) if out is None else _check(out, "out", q.shape, q.dtype, q.device)
+    st = lib.attn_decode_noalloc(_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                                 _dev(kv_lens, "kv_lens"), L, _dtype_code(q), B, hq, hkv, d, _scale(scale, d),
+                                 0 if num_splits is None else int(num_splits), _dev(out, "out"), _stream(q))
+    _lib.check("attn_decode_noalloc", st)
+    return out
 
 
 def decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, block_table: torch.Tensor,

@@ -28,6 +28,7 @@ STATUS_NAMES = {
     4: "ATTN_ERR_MISALIGNED",
     5: "ATTN_ERR_LAUNCH",
     6: "ATTN_ERR_TOO_LARGE",
+    7: "ATTN_ERR_SCRATCH",
 }
 ATTN_F16, ATTN_BF16 = 0, 1
 
@@ -50,6 +51,8 @@ SIGNATURES = {
     "attn_decode_splitk_q4": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                                        _c_int, _c_float, _c_int, _c_int, _vp, _vp, _vp, _vp]),
     "attn_kv_quantize_q4": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _c_int, _vp, _vp, _vp]),
+    "attn_decode_noalloc": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float,
+                                     _c_int, _vp, _vp]),
     "attn_merge_partials": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _c_int, _vp]),
     # measurement helpers (include/attn_calibrate.h)
     "attn_calib_mfma_bf16": (_c_int, [_vp, _c_int, _c_int, _vp]),

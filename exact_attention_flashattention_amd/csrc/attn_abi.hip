@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
+#include <mutex>
 
 #include "attn.h"
 #include "attn_calibrate.h"
@@ -40,6 +41,40 @@ int decode_max_chunk() {
   return v;
 }
 
+// ---- fixed scratch of attn_decode_noalloc: the split-K partial states live in
+// this array instead of caller memory.  Each GPU the library runs on holds its
+// own copy for the life of the process.  Host code never passes the array's
+// name to a kernel (on the host it names a stand-in, not device memory): the
+// device address is taken once per device with hipGetSymbolAddress and kept.
+static __device__ __align__(256) unsigned char scratch[ATTN_DECODE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 256;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Device address of this library's scratch array on the device `stream`
+// belongs to (the current device for the null stream).
+attn_status scratch_address(hipStream_t stream, void** out) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return ATTN_ERR_LAUNCH;
+  int dev = cur;
+  if (stream != nullptr && hipStreamGetDevice(stream, &dev) != hipSuccess) return ATTN_ERR_LAUNCH;
+  if (dev < 0 || dev >= kMaxDevices) return ATTN_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return ATTN_ERR_LAUNCH;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return ATTN_ERR_LAUNCH;
+    if (e != hipSuccess || p == nullptr) return ATTN_ERR_LAUNCH;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -53,6 +88,7 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_MISALIGNED: return "tensor pointer not 16-byte aligned";
     case ATTN_ERR_LAUNCH: return "kernel launch failed";
     case ATTN_ERR_TOO_LARGE: return "size beyond the kernels' index range";
+    case ATTN_ERR_SCRATCH: return "partial states larger than the library's fixed scratch buffer";
     default: return "unknown status";
   }
 }
@@ -134,6 +170,40 @@ attn_status attn_decode_splitk(const void* q, const void* k_cache, const void* v
   return from_hip(attn::launch_decode_splitk(q, k_cache, v_cache, kv_lens, max_kv_len, dtype == ATTN_BF16, batch, hq,
                                              hkv, d, scale, num_splits, chunk, part_m, part_l, part_o,
                                              static_cast<hipStream_t>(stream)));
+}
+
+attn_status attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const int* kv_lens,
+                                int max_kv_len, int dtype, int batch, int hq, int hkv, int d, float scale,
+                                int num_splits, void* o, void* stream) {
+  if (!q || !k_cache || !v_cache || !kv_lens || !o) return ATTN_ERR_NULL_PTR;
+  if (batch < 1 || hq < 1 || hkv < 1 || max_kv_len < 1 || num_splits < 0 || hq % hkv != 0 || !scale_ok(scale))
+    return ATTN_ERR_BAD_SHAPE;
+  if ((d != 64 && d != 128) || !dtype_ok(dtype)) return ATTN_ERR_UNSUPPORTED;
+  const int S = num_splits > 0 ? num_splits : attn_decode_num_splits(batch, hkv, max_kv_len);
+  const int groups = (hq / hkv + 15) / 16;
+  if ((long long)batch * hkv * max_kv_len * d >= kMaxElems || (long long)max_kv_len * d >= (1LL << 31) ||
+      batch > 65535 || (long long)hkv * groups > 65535 || S > 65535)
+    return ATTN_ERR_TOO_LARGE;
+  // partials in the scratch array: m [batch, hq, S], l [batch, hq, S], o [batch, hq, S, d], each 256-byte aligned
+  const size_t rows = (size_t)batch * hq * S;
+  const size_t off_l = align256(rows * sizeof(float));
+  const size_t off_o = off_l + align256(rows * sizeof(float));
+  if (off_o + rows * (size_t)d * sizeof(float) > ATTN_DECODE_NOALLOC_SCRATCH_BYTES) return ATTN_ERR_SCRATCH;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o)) return ATTN_ERR_MISALIGNED;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  void* base = nullptr;
+  const attn_status s = scratch_address(st, &base);
+  if (s != ATTN_OK) return s;
+  float* pm = static_cast<float*>(base);
+  float* pl = reinterpret_cast<float*>(static_cast<char*>(base) + off_l);
+  float* po = reinterpret_cast<float*>(static_cast<char*>(base) + off_o);
+  // every partial entry is written by the split-K kernel (an empty split writes (-inf, 0, 0)), so nothing
+  // left in the array by an earlier call is read
+  const int chunk = attn_decode_chunk_len(max_kv_len, S);
+  const hipError_t e = attn::launch_decode_splitk(q, k_cache, v_cache, kv_lens, max_kv_len, dtype == ATTN_BF16,
+                                                  batch, hq, hkv, d, scale, S, chunk, pm, pl, po, st);
+  if (e != hipSuccess) return ATTN_ERR_LAUNCH;
+  return from_hip(attn::launch_merge(pm, pl, po, batch * hq, d, S, dtype == ATTN_BF16, o, st));
 }
 
 attn_status attn_decode_splitk_paged(const void* q, const void* k_pages, const void* v_pages, const int* block_table,

@@ -14,8 +14,9 @@
  * ---------------------------------------
  * - Every tensor pointer is a device pointer, owned and allocated by the
  *   caller; every tensor is dense and row-major with the head dimension
- *   innermost.  The library never allocates or frees device memory and never
- *   synchronises.
+ *   innermost.  No call allocates or frees device memory, and none
+ *   synchronises.  (attn_decode_noalloc keeps its partial states in a fixed
+ *   array that the library holds on each GPU for the life of the process.)
  * - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Each
  *   call only enqueues kernels on it and returns.  ATTN_OK means the launches
  *   were accepted; faults during execution surface at the caller's next
@@ -49,7 +50,8 @@ typedef enum {
   ATTN_ERR_UNSUPPORTED = 3, /* d not in {64, 128}, or an unknown element type */
   ATTN_ERR_MISALIGNED = 4,  /* a tensor pointer is not 16-byte aligned */
   ATTN_ERR_LAUNCH = 5,      /* the HIP runtime rejected a kernel launch */
-  ATTN_ERR_TOO_LARGE = 6    /* a size exceeds what the kernels index (see each call) */
+  ATTN_ERR_TOO_LARGE = 6,   /* a size exceeds what the kernels index (see each call) */
+  ATTN_ERR_SCRATCH = 7      /* attn_decode_noalloc: partials exceed the fixed scratch buffer */
 } attn_status;
 
 typedef enum { ATTN_F16 = 0, ATTN_BF16 = 1 } attn_dtype;
@@ -276,6 +278,38 @@ attn_status attn_decode_splitk_q4(const void* q, const void* k_codes, const floa
  */
 attn_status attn_kv_quantize_q4(const void* x, int rows, int d, int dtype, int rotated, const int* out_rows,
                                 int out_capacity, void* codes, float* scales, void* stream);
+
+/*
+ * attn_decode_noalloc -- attn_decode_splitk followed by attn_merge_partials
+ * in one call that allocates nothing, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid allocation.  The split-K partial states live in a
+ * fixed scratch array inside the library (one per GPU, held until the
+ * process ends) instead of caller memory; the caller passes only inputs and
+ * the output.  No hipMalloc, hipFree or other allocating routine is called.
+ *
+ *   q, k_cache, v_cache, kv_lens, max_kv_len, dtype, batch, hq, hkv, d,
+ *   scale : as for attn_decode_splitk
+ *   num_splits : >= 1, or 0 for attn_decode_num_splits(batch, hkv, max_kv_len)
+ *   o          : [batch, hq, d] elements of `dtype`, DEVICE memory, written
+ *
+ * The partials -- batch·hq·num_splits·(d + 2) fp32 values, each of the three
+ * arrays 256-byte aligned -- must fit in ATTN_DECODE_NOALLOC_SCRATCH_BYTES
+ * (64 MiB; e.g. batch 64, hq 64, 16 splits, d 128 takes 34 MB), else
+ * ATTN_ERR_SCRATCH and nothing is launched.  Every call on one GPU uses the
+ * same array: calls that overlap on one GPU (on different streams, or from
+ * different threads without ordering) race and give undefined results.
+ * Nothing in the array needs to start at zero -- every partial the merge
+ * reads is written by the same call -- so a call never depends on what an
+ * earlier one left there.  The first call on a device looks up the array's
+ * address there (hipGetSymbolAddress); `stream` must belong to a device the
+ * library runs on.  Results are bit-identical to attn_decode_splitk +
+ * attn_merge_partials with the same num_splits.
+ */
+#define ATTN_DECODE_NOALLOC_SCRATCH_BYTES (64u << 20)
+attn_status attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const int* kv_lens,
+                                int max_kv_len, int dtype, int batch, int hq, int hkv, int d, float scale,
+                                int num_splits, void* o, void* stream);
 
 /*
  * attn_merge_partials -- merge the partial states of each (sequence, head)

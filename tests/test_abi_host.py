@@ -13,7 +13,7 @@ import pytest
 
 from exact_attention_flashattention_amd import _lib
 
-OK, NULL, SHAPE, UNSUP, MISAL, LAUNCH, BIG = range(7)
+OK, NULL, SHAPE, UNSUP, MISAL, LAUNCH, BIG, SCRATCH = range(8)
 BF16, F16 = _lib.ATTN_BF16, _lib.ATTN_F16
 P = 0x10000  # an aligned, non-null stand-in pointer (never dereferenced: every call below fails validation)
 
@@ -33,8 +33,8 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_status_strings(lib):
-    for code in range(7):
-        assert lib.attn_status_string(code)
+    for code in range(8):
+        assert lib.attn_status_string(code) and lib.attn_status_string(code) != b"unknown status"
     assert lib.attn_status_string(99) == b"unknown status"
 
 
@@ -198,6 +198,33 @@ def test_no_cpu_fallback_in_binding():
             assert "scaled_dot_product_attention" not in src
             for call in ("softmax(", ".exp(", "matmul", "bmm(", "einsum"):
                 assert call not in src, (fn, call)
+
+
+def noalloc(lib, q=P, kc=P, vc=P, lens=P, L=100, dtype=BF16, batch=1, hq=4, hkv=2, d=128, scale=0.1, S=2, o=P):
+    return lib.attn_decode_noalloc(q, kc, vc, lens, L, dtype, batch, hq, hkv, d, scale, S, o, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), NULL), (dict(kc=None), NULL), (dict(vc=None), NULL), (dict(lens=None), NULL), (dict(o=None), NULL),
+    (dict(batch=0), SHAPE), (dict(hq=3), SHAPE), (dict(L=0), SHAPE), (dict(S=-1), SHAPE),
+    (dict(scale=float("nan")), SHAPE), (dict(d=96), UNSUP), (dict(dtype=5), UNSUP),
+    (dict(q=P + 4), MISAL), (dict(o=P + 2), MISAL), (dict(S=70000), BIG),
+    # partial states beyond the 64 MiB scratch array: 64·64·64·130·4 B = 136 MB; and the plan's own count
+    (dict(batch=64, hq=64, hkv=8, L=32768, S=64), SCRATCH),
+    (dict(batch=256, hq=64, hkv=8, L=65536, S=0), SCRATCH),
+])
+def test_decode_noalloc_rejects_bad_arguments(lib, kw, status):
+    assert noalloc(lib, **kw) == status
+
+
+def test_decode_noalloc_scratch_limit_is_the_declared_one(lib):
+    """The largest accepted call fills at most ATTN_DECODE_NOALLOC_SCRATCH_BYTES: batch 64, hq 64 and 16 splits
+    at d=128 (34.1 MB, the ragged-decode shape) fit, and so do 31 splits (66.0 MB); 32 splits (68.2 MB) do not."""
+    hdr = open(_lib.HEADER_PATH).read()
+    assert "#define ATTN_DECODE_NOALLOC_SCRATCH_BYTES (64u << 20)" in hdr
+    assert noalloc(lib, batch=64, hq=64, hkv=8, L=32768, S=32, q=P + 4) == SCRATCH
+    for S in (16, 31):  # these fit, and fail only on the misaligned query pointer
+        assert noalloc(lib, batch=64, hq=64, hkv=8, L=32768, S=S, q=P + 4) == MISAL
 
 
 def test_calibration_helpers_reject_bad_arguments(lib):
