@@ -29,6 +29,8 @@ constexpr float kNegInf = -__builtin_huge_valf();
 // Storage element tags.  Both are 16-bit; they differ in the MFMA opcode and
 // in how fp32 is rounded back to storage.
 struct Bf16 {
+  static constexpr uint32_t kOnePair = 0x3F803F80u;  // (1.0, 1.0)
+  static constexpr uint32_t kBits256 = 0x4380u;      // 256.0
   static __device__ __forceinline__ uint32_t pack2(float a, float b) {
     bf16x2 v = {(__bf16)a, (__bf16)b};  // v_cvt_pk_bf16_f32: round to nearest even
     return __builtin_bit_cast(uint32_t, v);
@@ -49,6 +51,8 @@ struct Bf16 {
 };
 
 struct F16 {
+  static constexpr uint32_t kOnePair = 0x3C003C00u;  // (1.0, 1.0)
+  static constexpr uint32_t kBits256 = 0x5C00u;      // 256.0
   static __device__ __forceinline__ uint32_t pack2(float a, float b) {
     f16x2 v = {(_Float16)a, (_Float16)b};  // v_cvt_f16_f32: round to nearest even
     return __builtin_bit_cast(uint32_t, v);
@@ -143,6 +147,21 @@ __device__ __forceinline__ void lds_write16(char* base, uint32_t off, u32x4 x) {
 __device__ __forceinline__ u32x2 lds_read_tr16(const char* base, uint32_t off) {
   i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4*)(base + off));
   return __builtin_bit_cast(u32x2, r);
+}
+
+// Element-wise maximum of three packed pairs of 16-bit floats (v_pk_maximum3_f16).
+// Used on non-negative bf16 or fp16 bit patterns below 0x7C00, whose order as
+// fp16 values is the order of their bits, so it serves both types.  HI_FROM_LO
+// makes the high result take max(a.hi, b.lo, c.hi): the high half then holds
+// the largest of all four.
+template <bool HI_FROM_LO = false>
+__device__ __forceinline__ uint32_t pk_max3_16(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t r;
+  if (HI_FROM_LO)
+    asm("v_pk_maximum3_f16 %0, %1, %2, %3 op_sel_hi:[1,0,1]" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  else
+    asm("v_pk_maximum3_f16 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
 
 // exp2 on the transcendental unit (v_exp_f32); exp2(-inf) = 0.

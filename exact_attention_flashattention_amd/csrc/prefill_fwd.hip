@@ -39,9 +39,10 @@
 //     each lane 4 consecutive keys of one head-dimension column.
 //   * The softmax runs in the exp2 domain (scale·log2 e folded into one FMA
 //     per score, v_exp_f32).  The reference maximum is raised only when a
-//     row's new maximum exceeds it by more than 2^8; o and l share the
-//     reference, so o/l is unchanged and the output rescale stays off the
-//     common path.
+//     row's probabilities grow past 2^8; o and l share the reference, so o/l
+//     is unchanged and the output rescale stays off the common path.  At d=64
+//     the row sums l run on the matrix cores (one small MFMA per 16 keys), at
+//     d=128 on the vector unit (v_dot2 over the packed probabilities).
 //   * Causal: subtiles wholly above a wave's diagonal cost that wave nothing,
 //     the mask is applied only on subtiles that cross the diagonal or the
 //     sequence end (block classification of "Masking variants", "Attention
@@ -74,10 +75,6 @@
 namespace attn {
 
 namespace {
-
-// Largest probability (as a power of two) used without raising the reference
-// maximum, and the matching bound on a lane's 16-key probability sum.
-constexpr float kRescaleSum = 256.f;  // 2^8
 
 // NB 32-row query blocks per wave: two at d=64; one at d=128, where two
 // blocks' accumulators and Q operands would not fit two waves per SIMD.
@@ -416,11 +413,31 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   }
 
-  float m_run[NB], l_run[NB];
   f32x16 oacc[NB][DT];
+  // Row sums l.  At d=64, where the vector unit sets the pace, on the matrix
+  // cores: one 16x16x32 MFMA per 16-key k-step with the probabilities as its B
+  // operand.  Read that way, lane i's 8 values sit in column i % 16 at
+  // k = 8·(i / 16) .. +7, so column c mixes query c (lane groups 0 and 2, the
+  // two key halves) and query c + 16 (groups 1 and 3).  The A operand `ones`
+  // sums groups {0, 2} into output rows 0 and 8 and groups {1, 3} into rows 4
+  // and 12; output row 4·(i / 16) lands in lane i, so element 0 of every
+  // lane's accumulator is its own query's row sum (lanes q and q + 32 alike).
+  // The other elements stay 0.  At d=128 the extra MFMAs and registers cost
+  // more than the vector work they save (measured), and l is summed from the
+  // packed probabilities by v_dot2 in the vector step instead.
+  constexpr bool kMatSum = D == 64;
+  float l_run[NB];  // d=128: this lane's half of the row sum (16 of every 32 keys)
+  u32x4 ones;
+  {
+    const int m = lane & 15, g = lane >> 4;
+    const bool on = (g & 1) ? (m == 4 || m == 12) : (m == 0 || m == 8);
+    const uint32_t w = on ? T::kOnePair : 0u;
+    ones = u32x4{w, w, w, w};
+  }
+  f32x4 lsum[NB];
 #pragma unroll
   for (int blk = 0; blk < NB; ++blk) {
-    m_run[blk] = kNegInf;
+    lsum[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
     l_run[blk] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -492,6 +509,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   };
 
+  auto rowsum = [&]() ATTN_INLINE {
+    if constexpr (!kMatSum) return;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk) lsum[blk] = T::mfma16(ones, pf[blk][ks], lsum[blk]);
+  };
   auto pv = [&]() ATTN_INLINE {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -499,6 +523,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk) oacc[blk][dt] = T::mfma32(vf[dt][ks], pf[blk][ks], oacc[blk][dt]);
+    rowsum();
   };
   // P·V of the staged V operand while the V operand of subtile sb of tile t is
   // read into the same registers, each fragment right after its last use
@@ -516,6 +541,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);  // the MFMA(s) ...
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // ... then the two reads
       }
+    rowsum();
   };  // The next V operand is read between the P·V MFMAs at d=128; at d=64, whose
   // vector steps are the longer ones, after all of the step's MFMAs (measured).
   auto pv_then_load_v = [&](auto stg, int sb) ATTN_INLINE {
@@ -529,29 +555,39 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
 
   // probabilities of the subtile starting at key s0, rounded to the storage
-  // type as the B operands of P·V, and their row sums.  The exponentials use the
-  // current reference m_run (the largest row maximum seen when it was last
-  // raised).  The reference is raised -- to the row maximum so far, with l and
-  // o rescaled by exp2(m_run - m_new) -- and the subtile recomputed only when
-  // some lane's 16 probabilities sum past 2^8, or on a row's first
-  // subtile (no reference yet).  Every probability used is therefore at most
-  // 2^8 and the row maximum is at most 8 above the
-  // reference, so nothing overflows or loses precision; o and l share the
-  // reference, so o/l is the same either way.
-  // The row sum is accumulated in two dot2 chains, one of them starting from
-  // l itself (measured: 1 % faster than four chains added to l afterwards).
-  constexpr int NCH = 2;
-  float neg_ref[NB], lim[NB];  // -m_run (0 while m_run = -inf); the row-sum limit (-1 forces a raise)
+  // type as the B operands of P·V (and, at d=64, of the row-sum MFMAs).  The
+  // exponentials use the row's current reference m (the largest row maximum
+  // seen when it was last raised), kept as neg_ref = -m.  The reference is
+  // raised -- to the row maximum so far, with o and l rescaled by
+  // exp2(m - m_new) -- and the subtile recomputed only when some probability
+  // of the wave grows too large, or on a row's first subtile with a visible
+  // key (no reference yet).  Every probability used is therefore bounded and
+  // the row maximum at most 8 above the reference, so nothing overflows or
+  // loses precision; o and l share the reference, so o/l is the same either
+  // way.  The raise test:
+  //   d=64  -- some probability above 2^8.  The lane's largest rounded
+  //            probability comes from a packed-max tree over the pairs (their
+  //            bit patterns order like their values), lands in the high half
+  //            of a 32-bit word and is compared with 256 there, as unsigned
+  //            words.  A row without a reference holds neg_ref = +inf: its
+  //            exponentials are +inf (visible keys) or NaN (masked ones), whose
+  //            patterns -- NaN of either sign included -- pass the threshold.
+  //   d=128 -- the lane's 16 probabilities summing past 2^8, the sum taken
+  //            with the row sum itself (two v_dot2 chains, one of them starting
+  //            from l); `lim` = -1 forces the raise while the row has no
+  //            reference (neg_ref = 0 then).
+  constexpr uint32_t kRaiseLimit = (T::kBits256 << 16) | 0xFFFFu;
+  constexpr float kRescaleSum = 256.f;
+  float neg_ref[NB], lim[NB];
 #pragma unroll
   for (int blk = 0; blk < NB; ++blk) {
-    neg_ref[blk] = 0.f;
+    neg_ref[blk] = kMatSum ? __builtin_huge_valf() : 0.f;
     lim[blk] = -1.f;
   }
-  auto probs = [&](int blk, float nref, float acc) ATTN_INLINE {  // acc + this lane's 16 rounded probabilities
-    float ps[NCH];
-    ps[0] = acc;
-#pragma unroll
-    for (int i = 1; i < NCH; ++i) ps[i] = 0.f;
+  // the lane's 16 rounded probabilities into pf[blk]; returns, at d=64, their
+  // largest (high half of the word), at d=128 acc plus their sum
+  auto probs = [&](int blk, float nref, float acc) ATTN_INLINE {
+    float ps[2] = {acc, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -559,12 +595,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const float a0 = fast_exp2(fmaf(s[blk][8 * ks + 2 * i], c, nref));
         const float a1 = fast_exp2(fmaf(s[blk][8 * ks + 2 * i + 1], c, nref));
         pf[blk][ks][i] = T::pack2(a0, a1);
-        ps[(4 * ks + i) % NCH] = T::add_pair(ps[(4 * ks + i) % NCH], pf[blk][ks][i]);
+        if constexpr (!kMatSum) ps[i & 1] = T::add_pair(ps[i & 1], pf[blk][ks][i]);
       }
-    float r = ps[0];
-#pragma unroll
-    for (int i = 1; i < NCH; ++i) r += ps[i];
-    return r;
+    if constexpr (kMatSum) {
+      uint32_t t = pk_max3_16(pf[blk][0][0], pf[blk][0][1], pf[blk][0][2]);
+      t = pk_max3_16(t, pf[blk][0][3], pf[blk][1][0]);
+      t = pk_max3_16(t, pf[blk][1][1], pf[blk][1][2]);
+      t = pk_max3_16(t, pf[blk][1][3], t);
+      return __uint_as_float(pk_max3_16<true>(t, t, t));
+    } else {
+      return ps[0] + ps[1];
+    }
   };
   auto softmax = [&](int s0) ATTN_INLINE {
     if (s0 + 32 > nk || (CAUSAL && s0 + 31 > qw + off) ||
@@ -600,12 +641,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int e = 0; e < 16; ++e) s[blk][e] += fmaf(alibi_raw, (float)(16 * (e >> 3) + (e & 7)), base);
       }
     }
-    float lnew[NB];
     bool grow = false;
+    float lnew[NB];
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
       lnew[blk] = probs(blk, neg_ref[blk], l_run[blk]);
-      grow |= !(lnew[blk] - l_run[blk] <= lim[blk]);  // the subtile's sum; also true if infinite or NaN
+      if constexpr (kMatSum)
+        grow |= __float_as_uint(lnew[blk]) > kRaiseLimit;  // also for inf or NaN
+      else
+        grow |= !(lnew[blk] - l_run[blk] <= lim[blk]);  // the subtile's sum
     }
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
@@ -615,20 +659,29 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int i = 0; i < 5; ++i) m3[i] = fmaxf(fmaxf(s[blk][3 * i], s[blk][3 * i + 1]), s[blk][3 * i + 2]);
         m3[5] = s[blk][15];
         const float mx = fmaxf(fmaxf(fmaxf(m3[0], m3[1]), m3[2]), fmaxf(fmaxf(m3[3], m3[4]), m3[5]));
-        const float m_new = fmaxf(m_run[blk], max_xor32(mx) * c);
+        // the current reference (-inf while the row has none)
+        const float m_old = kMatSum ? (neg_ref[blk] == __builtin_huge_valf() ? kNegInf : -neg_ref[blk])
+                                    : (lim[blk] < 0.f ? kNegInf : -neg_ref[blk]);
+        const float m_new = fmaxf(m_old, max_xor32(mx) * c);
         const float ref = m_new == kNegInf ? 0.f : m_new;  // a row with no live key stays empty
-        const float alpha = fast_exp2(m_run[blk] - ref);
+        const float alpha = fast_exp2(m_old - ref);
+        lsum[blk][0] *= alpha;
         l_run[blk] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) oacc[blk][dt] *= alpha;
-        m_run[blk] = m_new;
-        neg_ref[blk] = -ref;
-        lim[blk] = m_new == kNegInf ? -1.f : kRescaleSum;
+        if constexpr (kMatSum) {
+          neg_ref[blk] = m_new == kNegInf ? __builtin_huge_valf() : -ref;
+        } else {
+          neg_ref[blk] = -ref;
+          lim[blk] = m_new == kNegInf ? -1.f : kRescaleSum;
+        }
         lnew[blk] = probs(blk, -ref, l_run[blk]);
       }
     }
+    if constexpr (!kMatSum) {
 #pragma unroll
-    for (int blk = 0; blk < NB; ++blk) l_run[blk] = lnew[blk];
+      for (int blk = 0; blk < NB; ++blk) l_run[blk] = lnew[blk];
+    }
   };
 
   // results of a vector step (probabilities and running statistics) and of a
@@ -638,16 +691,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int blk = 0; blk < NB; ++blk) {
       pin(pf[blk][0]);
       pin(pf[blk][1]);
-      pin(l_run[blk]);
-      pin(m_run[blk]);
       pin(neg_ref[blk]);
-      pin(lim[blk]);
+      if constexpr (!kMatSum) {
+        pin(l_run[blk]);
+        pin(lim[blk]);
+      }
     }
   };
   auto pin_matrix_step = [&]() ATTN_INLINE {
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
       pin(s[blk]);
+      if constexpr (kMatSum) pin(lsum[blk]);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) pin(oacc[blk][dt]);
     }
@@ -750,7 +805,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   float inv[NB];
 #pragma unroll
   for (int blk = 0; blk < NB; ++blk) {
-    const float l_tot = sum_xor32(l_run[blk]);
+    // d=64: both key halves (lanes q and q + 32 hold the same sum); d=128: add the other half
+    const float l_tot = kMatSum ? lsum[blk][0] : sum_xor32(l_run[blk]);
     inv[blk] = l_tot > 0.f ? 1.f / l_tot : 0.f;
   }
   store_rows([&](int blk, int dt, int e) ATTN_INLINE { return oacc[blk][dt][e] * inv[blk]; });
