@@ -117,13 +117,20 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // The destination is `lds_base + OFF`, added straight into M0.
 template <uint32_t OFF>
 __device__ __forceinline__ void dma16_to_lds(i32x4 rsrc, uint32_t voffset, uint32_t lds_base) {
-  // One wait state between the M0 write and the LDS-DMA that reads it.  M0 is
-  // not listed as clobbered (the compiler rejects that for a reserved
-  // register); the compiler itself writes M0 right before any instruction of
-  // its own that reads it, so nothing it holds there lives across this one.
+  // Wait states before the load: a buffer load must not read an SGPR that a
+  // vector instruction wrote fewer than 5 wait states earlier (the resource
+  // words come from v_readfirstlane, and the compiler may reload spilled
+  // scalars with v_readlane right before this statement), and the compiler
+  // does not check that hazard for inline assembly -- so the M0 write and
+  // s_nop 3 give 5 here, whatever precedes (with fewer, a v_readlane two wait
+  // states before a load has been seen to give wrong results).  The M0 write
+  // needs one of them too.  M0 is not listed as clobbered (the compiler
+  // rejects that for a reserved register); the compiler itself writes M0
+  // right before any instruction of its own that reads it, so nothing it
+  // holds there lives across this one.
   asm volatile(
       "s_add_u32 m0, %2, %3\n\t"
-      "s_nop 0\n\t"
+      "s_nop 3\n\t"
       "buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voffset),
       "s"(rsrc), "s"(lds_base), "n"(OFF)
       : "memory");
