@@ -127,13 +127,16 @@ __device__ __forceinline__ void dma16_to_lds(i32x4 rsrc, uint32_t voffset, uint3
   // needs one of them too.  M0 is not listed as clobbered (the compiler
   // rejects that for a reserved register); the compiler itself writes M0
   // right before any instruction of its own that reads it, so nothing it
-  // holds there lives across this one.
+  // holds there lives across this one.  The scalar add also writes the
+  // condition code SCC, which must be listed: otherwise the compiler may
+  // keep a carry or a comparison in SCC across the statement (a 64-bit
+  // pointer increment split around it lost its carry that way).
   asm volatile(
       "s_add_u32 m0, %2, %3\n\t"
       "s_nop 3\n\t"
       "buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voffset),
       "s"(rsrc), "s"(lds_base), "n"(OFF)
-      : "memory");
+      : "memory", "scc");
 }
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 

@@ -7,9 +7,11 @@ vector instruction (``v_readfirstlane``, or ``v_readlane`` reloading a
 spilled scalar) wrote fewer than 5 wait states earlier; the loads carry those
 wait states themselves.  This test compiles the kernels to assembly and scans
 every such load: no vector write of one of its scalar operands may sit within
-5 wait states before it.  It also checks that no kernel spills registers to
-scratch memory inside its main loops, and that no scalar store, scalar atomic
-or scalar-cache write-back is generated.
+5 wait states before it.  The same statements write the condition code SCC
+(their M0 add): no value the compiler put in SCC may be read after one of
+them before SCC is written again.  It also checks that no kernel spills
+registers to scratch memory inside its main loops, and that no scalar store,
+scalar atomic or scalar-cache write-back is generated.
 """
 
 import os
@@ -86,6 +88,41 @@ def test_lds_dma_loads_have_their_wait_states(asm):
             j -= 1
     assert loads > 100, "no LDS-DMA loads found: the scan is not looking at the prefill kernels"
     assert bad == 0
+
+
+_SCC_READERS = re.compile(r"s_(cbranch_scc[01]|cselect_b(32|64)|addc_u32|subb_u32|cmov_b(32|64)|cmovk_i32)$")
+_SCC_WRITERS = re.compile(r"s_(add|sub|addc|subb|and|or|xor|andn2|orn2|nand|nor|xnor|lshl|lshr|ashr|bfe|cmp|min|max|"
+                          r"not|abs|absdiff|bcnt|lshl[1-4]_add|quadmask|wqm|bitcmp)[_0-9a-z]*$")
+
+
+def test_inline_assembly_does_not_cut_through_scc(asm):
+    """Every inline-assembly block that writes SCC must be followed, on the
+    straight-line path after it, by a write of SCC before any read: a read
+    first would see the block's value instead of the one the compiler put
+    there."""
+    blocks = 0
+    for src, lines in asm.items():
+        for i, line in enumerate(lines):
+            if line.strip() != ";;#ASMSTART":
+                continue
+            j, body = i + 1, []
+            while lines[j].strip() != ";;#ASMEND":
+                body.append(lines[j].strip())
+                j += 1
+            if not any(_SCC_WRITERS.match(b.split()[0]) for b in body if b):
+                continue
+            blocks += 1
+            for line2 in lines[j + 1:]:
+                s = line2.split(";")[0].strip()
+                if not s or s.startswith("."):
+                    continue
+                if s.endswith(":"):
+                    break  # a label: another path may join here; the path through the block ends
+                op = s.split()[0]
+                assert not _SCC_READERS.match(op), f"{src}: {s!r} reads SCC written by inline assembly"
+                if _SCC_WRITERS.match(op):
+                    break
+    assert blocks > 100, "no SCC-writing inline assembly found: the scan is not looking at the DMA loads"
 
 
 def test_no_scalar_memory_writes(asm):
