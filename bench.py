@@ -547,7 +547,7 @@ def main() -> int:
             vq, vs = A.kv_quantize_q4(vc, True)
             del kc, vc
             copies.append((q, kq, ks, vq, vs, lens.to(dev)))
-        S = A.decode_num_splits(w.batch, w.hkv, w.max_kv_len)
+        S = A.decode_q4_num_splits(w.batch, w.hkv, w.max_kv_len)
         part = partials(w, S)
         out = torch.empty((w.batch, w.hq, w.d), dtype=torch.bfloat16, device=dev)
         total = int(copies[0][5].sum())

@@ -20,7 +20,7 @@ Entry points (same names as the C ABI):
 * ``decode(...)``, ``decode_paged(...)``, ``decode_q4(...)`` -- split-K then merge, back to back on one stream
 * ``decode_noalloc(q, k_cache, v_cache, kv_lens, num_splits, scale)`` -- ``attn_decode_noalloc``: the same
   split-K and merge with the partial states in the library's fixed scratch array (no workspace)
-* ``decode_num_splits``, ``decode_chunk_len``, ``decode_workspace_bytes`` -- host helpers
+* ``decode_num_splits``, ``decode_q4_num_splits``, ``decode_chunk_len``, ``decode_workspace_bytes`` -- host helpers
 """
 
 from __future__ import annotations
@@ -35,7 +35,7 @@ from ._lib import ATTN_BF16, ATTN_F16, AttnError  # noqa: F401
 
 __all__ = ["prefill_fwd", "prefill_varlen_fwd", "decode_splitk", "decode_splitk_paged", "decode_splitk_q4", "decode_q4",
            "kv_quantize_q4", "merge_partials", "decode", "decode_paged", "decode_noalloc",
-           "decode_num_splits", "decode_chunk_len", "decode_workspace_bytes", "AttnError"]
+           "decode_num_splits", "decode_q4_num_splits", "decode_chunk_len", "decode_workspace_bytes", "AttnError"]
 
 _DTYPES = {torch.bfloat16: ATTN_BF16, torch.float16: ATTN_F16}
 
@@ -156,6 +156,10 @@ def decode_num_splits(batch: int, hkv: int, max_kv_len: int) -> int:
     return int(_lib_handle().attn_decode_num_splits(batch, hkv, max_kv_len))
 
 
+def decode_q4_num_splits(batch: int, hkv: int, max_kv_len: int) -> int:
+    return int(_lib_handle().attn_decode_q4_num_splits(batch, hkv, max_kv_len))
+
+
 def decode_chunk_len(max_kv_len: int, num_splits: int) -> int:
     return int(_lib_handle().attn_decode_chunk_len(max_kv_len, num_splits))
 
@@ -237,7 +241,7 @@ def decode_splitk_q4(q: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Ten
     if kv_lens.dtype != torch.int32 or kv_lens.numel() != B or kv_lens.device != q.device:
         raise ValueError("kv_lens must be an int32 device tensor with one entry per sequence")
     _same_device(q, k_codes=k_codes, v_codes=v_codes, k_scales=k_scales, v_scales=v_scales)
-    S = decode_num_splits(B, hkv, L) if num_splits is None else int(num_splits)
+    S = decode_q4_num_splits(B, hkv, L) if num_splits is None else int(num_splits)
     pm, pl, po = _partials(partials, B, hq, S, d, q.device)
     st = lib.attn_decode_splitk_q4(_dev(q, "q"), _dev(k_codes, "k_codes"), _dev(k_scales, "k_scales"),
                                    _dev(v_codes, "v_codes"), _dev(v_scales, "v_scales"), _dev(kv_lens, "kv_lens"), L,

@@ -41,6 +41,7 @@ SIGNATURES = {
     "attn_prefill_varlen_fwd": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                                          _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _c_int, _vp, _vp]),
     "attn_decode_num_splits": (_c_int, [_c_int, _c_int, _c_int]),
+    "attn_decode_q4_num_splits": (_c_int, [_c_int, _c_int, _c_int]),
     "attn_decode_chunk_len": (_c_int, [_c_int, _c_int]),
     "attn_decode_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int]),
     "attn_decode_splitk": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float,

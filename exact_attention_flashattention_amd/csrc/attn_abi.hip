@@ -13,8 +13,18 @@
 namespace {
 
 constexpr long long kMaxElems = 1LL << 40;  // per-tensor element bound the kernels' 64-bit offsets assume
-constexpr int kDecodeTargetWaves = 2048;    // decode waves that fill 256 CUs at 8 waves per CU
-constexpr int kDecodeMaxChunk = 2048;       // most keys per split, so ragged lengths balance across waves
+// Split plans.  bf16/fp16 caches: about 512 waves of up to 4096 keys each --
+// two per CU, each streaming 1 MB of K and V at d = 128 -- read the cache
+// faster than more, shorter splits (measured on one sequence of 262144 keys,
+// 8 KV heads: 64 splits 5.9 TB/s by wall clock with the merge, 256 splits
+// 5.7; on 64 ragged sequences of up to 32768 keys 8 and 16 splits tie).  The
+// 4-bit cache's kernel does more arithmetic per byte and needs more waves in
+// flight: about 2048 waves of up to 2048 keys (64 splits there: 2.9 TB/s of
+// codes and scales, 256 splits: 4.4).
+constexpr int kDecodeTargetWaves = 512;
+constexpr int kDecodeMaxChunk = 4096;       // most keys per split, so ragged lengths balance across waves
+constexpr int kDecodeQ4TargetWaves = 2048;
+constexpr int kDecodeQ4MaxChunk = 2048;
 constexpr int kDecodeMinChunk = 256;        // fewest keys worth a split of its own
 constexpr int kChunkAlign = 64;
 
@@ -125,19 +135,29 @@ attn_status attn_prefill_varlen_fwd(const void* q, const void* k, const void* v,
                                               causal != 0, window, alibi_slopes, static_cast<hipStream_t>(stream)));
 }
 
-int attn_decode_num_splits(int batch, int hkv, int max_kv_len) {
+namespace {
+int split_plan(int batch, int hkv, int max_kv_len, int target_waves, int max_chunk) {
   if (batch < 1 || hkv < 1 || max_kv_len < 1) return 1;
   // enough splits to fill the GPU, and enough that no split holds more than
   // the maximum chunk; never so many that splits drop below the minimum chunk
   const long long heads = (long long)batch * hkv;
-  const long long fill = (decode_target_waves() + heads - 1) / heads;
-  const long long bound = (max_kv_len + decode_max_chunk() - 1) / decode_max_chunk();
+  const long long fill = (target_waves + heads - 1) / heads;
+  const long long bound = (max_kv_len + max_chunk - 1) / max_chunk;
   const long long useful = (max_kv_len + kDecodeMinChunk - 1) / kDecodeMinChunk;
   long long s = fill > bound ? fill : bound;
   if (s > useful) s = useful;
   if (s < 1) s = 1;
   if (s > 65535) s = 65535;
   return (int)s;
+}
+}  // namespace
+
+int attn_decode_num_splits(int batch, int hkv, int max_kv_len) {
+  return split_plan(batch, hkv, max_kv_len, decode_target_waves(), decode_max_chunk());
+}
+
+int attn_decode_q4_num_splits(int batch, int hkv, int max_kv_len) {
+  return split_plan(batch, hkv, max_kv_len, kDecodeQ4TargetWaves, kDecodeQ4MaxChunk);
 }
 
 int attn_decode_chunk_len(int max_kv_len, int num_splits) {

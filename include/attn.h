@@ -137,8 +137,13 @@ attn_status attn_prefill_varlen_fwd(const void* q, const void* k, const void* v,
  * where C = attn_decode_chunk_len(max_kv_len, num_splits).
  */
 
-/* A split count that fills the GPU for this shape (host heuristic, >= 1). */
+/* A split count that reads a bf16/fp16 cache of this shape fastest (host
+ * heuristic, >= 1): about 512 waves, at most 4096 keys per split. */
 int attn_decode_num_splits(int batch, int hkv, int max_kv_len);
+
+/* The same for the 4-bit cache of attn_decode_splitk_q4, whose kernel needs
+ * more waves in flight: about 2048 waves, at most 2048 keys per split. */
+int attn_decode_q4_num_splits(int batch, int hkv, int max_kv_len);
 
 /* Keys per split C for the given split count (a multiple of 64, >= 64);
  * returns 0 if max_kv_len < 1 or num_splits < 1. */

@@ -155,16 +155,21 @@ def test_merge_rejects_bad_arguments(lib, args, status):
 
 
 def test_decode_split_plan(lib):
-    # one sequence, 8 KV heads, 262144 keys: enough splits to give every CU several waves
+    # one sequence, 8 KV heads, 262144 keys: about 512 waves of at most 4096 keys
     s = lib.attn_decode_num_splits(1, 8, 262144)
-    assert 8 * s >= 2048
+    assert s == 64 and 8 * s >= 512
     c = lib.attn_decode_chunk_len(262144, s)
-    assert c % 64 == 0 and c * s >= 262144 and c * (s - 1) < 262144
+    assert c % 64 == 0 and c * s >= 262144 and c * (s - 1) < 262144 and c <= 4096
     # many sequences already fill the GPU: splits only bound the keys per split
     s = lib.attn_decode_num_splits(64, 8, 32768)
-    assert s <= 32 and lib.attn_decode_chunk_len(32768, s) <= 4096
+    assert s == 8 and lib.attn_decode_chunk_len(32768, s) <= 4096
     assert lib.attn_decode_num_splits(1, 1, 10) == 1
     assert lib.attn_decode_num_splits(0, 8, 10) == 1
+    # the 4-bit cache: about 2048 waves of at most 2048 keys
+    s = lib.attn_decode_q4_num_splits(1, 8, 262144)
+    assert s == 256 and lib.attn_decode_chunk_len(262144, s) <= 2048
+    assert lib.attn_decode_q4_num_splits(64, 8, 32768) == 16
+    assert lib.attn_decode_q4_num_splits(1, 1, 10) == 1 and lib.attn_decode_q4_num_splits(0, 8, 10) == 1
     for L in (1, 63, 64, 65, 1000, 262144):
         for S in (1, 2, 7, 100):
             c = lib.attn_decode_chunk_len(L, S)

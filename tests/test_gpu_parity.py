@@ -152,6 +152,41 @@ def test_prefill_n4096_whole_output(A, name):
     assert_close(out, ref, f"{w.name} (whole output)")
 
 
+@pytest.mark.parametrize("B,hq,hkv,n,d,causal,dtype", [
+    (5, 20, 4, 2048, 128, False, "bf16"),   # 100 (batch, head) pairs: not a multiple of the 8 XCDs
+    (5, 20, 4, 2048, 128, True, "bf16"),
+    (6, 16, 16, 4096, 64, True, "f16"),
+    (9, 8, 2, 4096, 64, False, "bf16"),
+    (3, 24, 8, 2560, 128, True, "f16"),     # longest-first causal items of 10 different lengths
+])
+def test_prefill_many_items_per_compute_unit(A, B, hq, hkv, n, d, causal, dtype):
+    """Square problems with several work items per compute unit, head counts that do not divide by the
+    8 XCDs and GQA: the whole output equals, bit for bit, the varlen kernel's on the same rows (same
+    tiles, same arithmetic, another work mapping), and a row sample of every (batch, head) slice -- the
+    first and last 32 rows and 32 random ones -- matches the oracle."""
+    w = workloads.Prefill(f"many_items_{B}_{hq}_{hkv}_{n}_{d}_{int(causal)}_{dtype}", B, hq, hkv, n, d, causal, dtype)
+    announce(w.name)
+    q, k, v = (t.to(DEV) for t in workloads.prefill_inputs(w, salt=n + d))
+    sq = A.prefill_fwd(q, k, v, causal=causal, scale=w.scale)
+    cu = torch.arange(0, (B + 1) * n, n, dtype=torch.int32, device=DEV)
+    pq = q.transpose(1, 2).reshape(B * n, hq, d).contiguous()
+    pk = k.transpose(1, 2).reshape(B * n, hkv, d).contiguous()
+    pv = v.transpose(1, 2).reshape(B * n, hkv, d).contiguous()
+    ref_bits = A.prefill_varlen_fwd(pq, pk, pv, cu, cu, n, n, causal=causal, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(sq.transpose(1, 2).reshape(B * n, hq, d), ref_bits), "square kernel != varlen kernel"
+    rng = np.random.default_rng(n)
+    rows = np.unique(np.concatenate([np.arange(32), np.arange(n - 32, n), rng.integers(0, n, 32)]))
+    g = hq // hkv
+    got, ref = [], []
+    for b in range(B):
+        for h in range(hq):
+            K, V = f64(k[b, h // g]), f64(v[b, h // g])
+            ref.append(oracle.attention_rows(f64(q[b, h])[rows], K, V, w.scale, rows if causal else None))
+            got.append(f64(sq[b, h])[rows])
+    assert_close(np.concatenate(got), np.concatenate(ref), f"{w.name} (row sample of every slice)")
+
+
 def c3_sample_rows(n, rng):
     """The routine row sample of the causal N=32768 workload: every row of the first and last 256-row
     blocks, every row i with i mod 128 in {0, 127} (the first and last row of each 128-row block, where
@@ -609,7 +644,7 @@ def q4_case(A, w, kv_lens, max_len, batch, num_splits, rotated, seed=0, v_mult=N
     announce(f"q4 {w.name} B={batch} L={max_len} lens={kv_lens.tolist()[:6]} S={num_splits} rotated={rotated}")
     q, kq, ks, vq, vs, lens = q4cache.q4_inputs(w, rotated, DEV, salt=seed, kv_lens=kv_lens, max_kv_len=max_len,
                                                 batch=batch, v_mult=v_mult)
-    S = A.decode_num_splits(batch, w.hkv, max_len) if num_splits is None else num_splits
+    S = A.decode_q4_num_splits(batch, w.hkv, max_len) if num_splits is None else num_splits
     out = A.decode_q4(q, kq, ks, vq, vs, lens.to(DEV), rotated, S, w.scale)
     torch.cuda.synchronize()
     ref = oracle.decode_q4(f64(q), kq.cpu().numpy(), ks.cpu().double().numpy(), vq.cpu().numpy(),
