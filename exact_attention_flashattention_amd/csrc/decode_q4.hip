@@ -45,7 +45,7 @@ namespace attn {
 namespace {
 
 constexpr int kQStep = 32;  // keys per step
-constexpr int kQDepth = 4;  // steps in the load ring
+constexpr int kQDepth = 2;  // steps in the load ring
 constexpr float kQSlack = 8.f;  // log2 of the largest probability used without raising the reference
 
 template <class T>
@@ -346,8 +346,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   };
 
   // A ring of kQDepth steps: while step i is processed, steps i+1 .. i+kQDepth-1
-  // are in flight (a 4-bit step is a quarter of a 16-bit one, so one step ahead
-  // leaves the wave waiting on memory latency).
+  // are in flight.  With 2048 waves of eight small loads per step the memory
+  // pipeline, not the latency, sets the pace: one step ahead reads the cache
+  // faster than three (measured on 262144 positions: 4.5 against 4.3 TB/s by
+  // wall clock with the merge) and needs 66 fewer registers.
   // The loads are issued unconditionally (past the end they read nothing), so
   // the compiler can count the steps in flight and wait for the current one only.
   Q4Stage<D> st[kQDepth];
