@@ -305,6 +305,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   }
 }
 
+// LDS reserved by every decode workgroup beside its own small buffer, so that
+// at most two of them (two waves) share a compute unit: gfx950 has 160 KB of
+// LDS per CU and a workgroup then takes 64 KB + its ~10 KB.  Fewer concurrent
+// cache streams read HBM faster -- on 64 ragged sequences of up to 32768 keys
+// 5.84 TB/s against 5.60 with up to four per CU (one per SIMD), and one per CU
+// is too few (5.0); a single long sequence, whose 512 waves sit two per CU
+// anyway, is unchanged (measured).
+constexpr unsigned kDecodeLdsReserve = 64u * 1024u;
+
 template <class T, int D, bool PAGED>
 static hipError_t launch_decode_t(const void* q, const void* kc, const void* vc, const int* kv_lens, int max_kv_len,
                                   int batch, int hq, int hkv, float scale, int num_splits, int chunk, float* pm,
@@ -312,7 +321,7 @@ static hipError_t launch_decode_t(const void* q, const void* kc, const void* vc,
   const int g = hq / hkv;
   const int groups = (g + 15) / 16;
   dim3 grid(num_splits, hkv * groups, batch);
-  decode_splitk_kernel<T, D, PAGED><<<grid, dim3(64), 0, stream>>>(
+  decode_splitk_kernel<T, D, PAGED><<<grid, dim3(64), kDecodeLdsReserve, stream>>>(
       static_cast<const char*>(q), static_cast<const char*>(kc), static_cast<const char*>(vc), kv_lens, max_kv_len,
       hq, hkv, g, chunk, num_splits, scale * kLog2e, pm, pl, po, pt, mk);
   return hipGetLastError();
