@@ -3,7 +3,6 @@
 // Nothing here allocates, frees or synchronises device memory.
 #include <cmath>
 #include <cstdint>
-#include <cstdlib>
 #include <mutex>
 
 #include "attn.h"
@@ -33,23 +32,6 @@ bool dtype_ok(int t) { return t == ATTN_F16 || t == ATTN_BF16; }
 bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
 
 attn_status from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH; }
-
-// Optional overrides of the split heuristic for A/B measurements:
-// ATTN_DECODE_TARGET_WAVES=<n> (waves to aim for) and ATTN_DECODE_MAX_CHUNK=<n>
-// (most keys per split).  Read once per process.
-int env_int(const char* name, int fallback) {
-  const char* s = std::getenv(name);
-  const long x = s ? std::strtol(s, nullptr, 10) : 0;
-  return (x > 0 && x < (1L << 24)) ? (int)x : fallback;
-}
-int decode_target_waves() {
-  static const int v = env_int("ATTN_DECODE_TARGET_WAVES", kDecodeTargetWaves);
-  return v;
-}
-int decode_max_chunk() {
-  static const int v = env_int("ATTN_DECODE_MAX_CHUNK", kDecodeMaxChunk);
-  return v;
-}
 
 // ---- fixed scratch of attn_decode_noalloc: the split-K partial states live in
 // this array instead of caller memory.  Each GPU the library runs on holds its
@@ -153,7 +135,7 @@ int split_plan(int batch, int hkv, int max_kv_len, int target_waves, int max_chu
 }  // namespace
 
 int attn_decode_num_splits(int batch, int hkv, int max_kv_len) {
-  return split_plan(batch, hkv, max_kv_len, decode_target_waves(), decode_max_chunk());
+  return split_plan(batch, hkv, max_kv_len, kDecodeTargetWaves, kDecodeMaxChunk);
 }
 
 int attn_decode_q4_num_splits(int batch, int hkv, int max_kv_len) {
