@@ -801,7 +801,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   tile_steps(nkt - 1, (nkt - 1) % S, std::true_type{});
   if (grp == 0) step_end<true>();
 
-  // ---- epilogue: O = o / l, rounded to the storage type, written once
+  // ---- epilogue: O = o / l, rounded to the storage type, written once.
+  // Every LDS read and tile transfer has completed before the barrier just
+  // passed, so the tile buffers are free: each wave stages its rows (32·NB of
+  // them, contiguous in O) in its own 8 KB of LDS and writes them back as
+  // whole 1 KB runs instead of 16-byte pieces of 32 rows per instruction.
   float inv[NB];
 #pragma unroll
   for (int blk = 0; blk < NB; ++blk) {
@@ -809,7 +813,33 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const float l_tot = kMatSum ? lsum[blk][0] : sum_xor32(l_run[blk]);
     inv[blk] = l_tot > 0.f ? 1.f / l_tot : 0.f;
   }
-  store_rows([&](int blk, int dt, int e) ATTN_INLINE { return oacc[blk][dt][e] * inv[blk]; });
+  constexpr uint32_t WAVE_OUT = 32 * NB * ROWB;  // bytes of this wave's output rows
+  static_assert(WAVE_OUT == 8192 && Cfg::WAVES * WAVE_OUT <= Cfg::LDS, "output staging fits the tile buffers");
+  char* ostage = lds + wave * WAVE_OUT;
+  // 16-byte chunk c of staged row r sits at chunk c ^ oswz(r): the 32 lanes of
+  // a half-wave write 8-byte halves of one chunk column across 16 rows, and
+  // read 16-byte chunks of whole rows, both without bank conflicts
+  auto oswz = [](int r) ATTN_INLINE { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
+#pragma unroll
+  for (int blk = 0; blk < NB; ++blk) {
+    const int r = 32 * blk + l32;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int eh = 0; eh < 4; ++eh) {  // columns 32·dt + 8·eh + 4·half .. +3 = half of chunk 4·dt + eh
+        const u32x2 w = {T::pack2(oacc[blk][dt][4 * eh + 0] * inv[blk], oacc[blk][dt][4 * eh + 1] * inv[blk]),
+                         T::pack2(oacc[blk][dt][4 * eh + 2] * inv[blk], oacc[blk][dt][4 * eh + 3] * inv[blk])};
+        *reinterpret_cast<u32x2*>(ostage + r * ROWB + (((4 * dt + eh) ^ oswz(r)) * 16) + 8 * half) = w;
+      }
+  }
+#pragma unroll
+  for (int i = 0; i < (int)(WAVE_OUT / 1024); ++i) {
+    const int byte = i * 1024 + lane * 16;
+    const int r = byte / ROWB, ch = (byte % ROWB) / 16;
+    const u32x4 x = lds_read16(ostage, r * ROWB + ((ch ^ oswz(r)) * 16));
+    const int qrow = qw + r;
+    if (qrow < nq) gstore16(o + qo_base + (size_t)qrow * q_stride + ch * 16, x);
+  }
 }
 
 template <class T, int D, bool CAUSAL, bool VARLEN>
