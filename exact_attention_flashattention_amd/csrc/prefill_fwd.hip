@@ -215,17 +215,55 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // takes its units one after another, each unit's query tiles from the last
   // down with the unit's query heads side by side, so the tiles that stream
   // the same K and V run close together and share them in the XCD's L2.
+  // A sequence's last query tile is usually partial; its rows fill only the
+  // first nb of the 8 waves' row blocks, and since the query heads of a unit
+  // see the same keys under the same mask, one workgroup takes that tile for
+  // P = min(g, 8 / nb) of them: wave w serves head w / nb, row block w % nb
+  // (waves left over hold no rows).  The unit's other tiles are whole.
   int b, h, qt;
+  int wrow = wave;   // this wave's row block within the query tile
+  bool live = true;  // false: a wave of a shared last tile with no head to serve
+  int nq = n, nk = n;
+  size_t qo_base, kv_base;
+  const uint32_t q_stride = VARLEN ? (uint32_t)hq * ROWB : ROWB;
+  const uint32_t kv_stride = VARLEN ? (uint32_t)hkv * ROWB : ROWB;
   if constexpr (VARLEN) {
     const int g = hq / hkv;
     const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
     const int units = (batch * hkv - xcd + 7) / 8;   // units of this XCD
-    const int per_unit = g * num_q_tiles;            // work items of one unit
+    const int per_unit = g * num_q_tiles;            // workgroups set aside per unit
     if (slot >= units * per_unit) return;            // (the whole workgroup)
     const int unit = xcd + 8 * (slot / per_unit);
-    qt = num_q_tiles - 1 - (slot % per_unit) / g;
+    const int j = slot % per_unit;                   // work item within the unit
     b = unit / hkv;
-    h = (unit % hkv) * g + (slot % per_unit) % g;
+    // rows of this sequence: nq queries, nk keys (bounds clamped into the buffers)
+    int qs = vl.cu_q[b], qe = vl.cu_q[b + 1], ks = vl.cu_k[b], ke = vl.cu_k[b + 1];
+    qs = min(max(qs, 0), vl.total_q);
+    qe = min(max(qe, qs), min(vl.total_q, qs + n));
+    ks = min(max(ks, 0), vl.total_k);
+    ke = min(max(ke, ks), min(vl.total_k, ks + vl.max_k));
+    nq = __builtin_amdgcn_readfirstlane(qe - qs);
+    nk = __builtin_amdgcn_readfirstlane(ke - ks);
+    const int tiles = (nq + Cfg::BR - 1) / Cfg::BR;
+    if (tiles == 0) return;
+    const int nb = (nq - (tiles - 1) * Cfg::BR + 32 * NB - 1) / (32 * NB);  // row blocks of the last tile
+    const int P = min(g, Cfg::WAVES / nb);  // query heads per workgroup on the last tile
+    const int np = (g + P - 1) / P;         // workgroups of the last tile
+    int head;
+    if (j < np) {
+      qt = tiles - 1;
+      wrow = wave % nb;
+      head = j * P + wave / nb;
+      live = wave / nb < P && head < g;
+      if (!live) head = j * P;
+    } else {
+      qt = tiles - 2 - (j - np) / g;
+      if (qt < 0) return;  // this unit has fewer tiles than the longest sequence (the whole workgroup)
+      head = (j - np) % g;
+    }
+    h = (unit % hkv) * g + head;
+    qo_base = ((size_t)qs * hq + h) * ROWB;
+    kv_base = ((size_t)ks * hkv + unit % hkv) * ROWB;
   } else {
     const int H = batch * hq;
     int bh;
@@ -245,32 +283,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     h = bh % hq;
     b = bh / hq;
-  }
-  const int kvh = h / (hq / hkv);
-
-  const int q0 = qt * Cfg::BR;
-  const int qw = q0 + wave * 32 * NB;  // first query row of this wave; block blk covers qw + 32·blk ..
-  // Rows of this (sequence, head): nq queries, nk keys, byte offsets of row 0
-  // and row strides.  The causal diagonal is shifted by off = nk - nq.
-  int nq = n, nk = n;
-  size_t qo_base, kv_base;
-  const uint32_t q_stride = VARLEN ? (uint32_t)hq * ROWB : ROWB;
-  const uint32_t kv_stride = VARLEN ? (uint32_t)hkv * ROWB : ROWB;
-  if constexpr (VARLEN) {
-    int qs = vl.cu_q[b], qe = vl.cu_q[b + 1], ks = vl.cu_k[b], ke = vl.cu_k[b + 1];
-    qs = min(max(qs, 0), vl.total_q);
-    qe = min(max(qe, qs), min(vl.total_q, qs + n));
-    ks = min(max(ks, 0), vl.total_k);
-    ke = min(max(ke, ks), min(vl.total_k, ks + vl.max_k));
-    nq = __builtin_amdgcn_readfirstlane(qe - qs);
-    nk = __builtin_amdgcn_readfirstlane(ke - ks);
-    if (q0 >= nq) return;  // past this sequence's last query tile (the whole workgroup)
-    qo_base = ((size_t)qs * hq + h) * ROWB;
-    kv_base = ((size_t)ks * hkv + kvh) * ROWB;
-  } else {
     qo_base = ((size_t)b * hq + h) * (size_t)n * ROWB;
-    kv_base = ((size_t)b * hkv + kvh) * (size_t)n * ROWB;
+    kv_base = ((size_t)b * hkv + h / (hq / hkv)) * (size_t)n * ROWB;
   }
+  // Query tile qt of this (sequence, head); the causal diagonal is shifted by
+  // off = nk - nq.  A wave with no rows starts at nq, past the last row.
+  const int q0 = qt * Cfg::BR;
+  const int qw = live ? q0 + wrow * 32 * NB : nq;  // first query row of this wave; block blk covers qw + 32·blk ..
   const int off = VARLEN ? nk - nq : 0;
   const char* kp = k + kv_base;
   const char* vp = v + kv_base;
