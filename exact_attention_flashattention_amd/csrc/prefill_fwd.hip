@@ -214,7 +214,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // alike -- and the query heads sharing a KV head stay on one XCD.  An XCD
   // takes its units one after another, each unit's query tiles from the last
   // down with the unit's query heads side by side, so the tiles that stream
-  // the same K and V run close together and share them in the XCD's L2.
+  // the same K and V run close together and share them in the XCD's L2.  The
+  // units go in order of key count, most first, so that the XCD's share ends
+  // on the shortest work items; their work items are numbered back to back,
+  // and the workgroups past the last one (the grid is sized for every unit
+  // having the longest sequence's tiles) come last and exit at once.  (With
+  // more than 64 units per XCD the units keep their index order, each given
+  // that many workgroups.)
   // A sequence's last query tile is usually partial; its rows fill only the
   // first nb of the 8 waves' row blocks, and since the query heads of a unit
   // see the same keys under the same mask, one workgroup takes that tile for
@@ -230,25 +236,62 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if constexpr (VARLEN) {
     const int g = hq / hkv;
     const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
-    const int units = (batch * hkv - xcd + 7) / 8;   // units of this XCD
-    const int per_unit = g * num_q_tiles;            // workgroups set aside per unit
-    if (slot >= units * per_unit) return;            // (the whole workgroup)
-    const int unit = xcd + 8 * (slot / per_unit);
-    const int j = slot % per_unit;                   // work item within the unit
+    const int units = (batch * hkv - xcd + 7) / 8;  // units of this XCD: xcd, xcd + 8, ...
+    // row bounds of sequence bb, clamped into the buffers
+    auto bounds = [&](int bb, int& qs_, int& qe_, int& ks_, int& ke_) ATTN_INLINE {
+      qs_ = min(max(vl.cu_q[bb], 0), vl.total_q);
+      qe_ = min(max(vl.cu_q[bb + 1], qs_), min(vl.total_q, qs_ + n));
+      ks_ = min(max(vl.cu_k[bb], 0), vl.total_k);
+      ke_ = min(max(vl.cu_k[bb + 1], ks_), min(vl.total_k, ks_ + vl.max_k));
+    };
+    // query tiles of nq_ rows; row blocks of the last one, query heads per
+    // workgroup on it, and its workgroups
+    auto tiling = [&](int nq_, int& tiles_, int& nb_, int& P_, int& np_) ATTN_INLINE {
+      tiles_ = (nq_ + Cfg::BR - 1) / Cfg::BR;
+      nb_ = max(1, (nq_ - (tiles_ - 1) * Cfg::BR + 32 * NB - 1) / (32 * NB));
+      P_ = min(g, Cfg::WAVES / nb_);
+      np_ = (g + P_ - 1) / P_;
+    };
+    int unit, j, qs, qe, ks, ke;
+    if (units <= 64) {
+      // lane l describes unit xcd + 8l: its bounds, key count and work items
+      int lqs = 0, lqe = 0, lks = 0, lke = 0, lnk = -1, items = 0;
+      if (lane < units) {
+        bounds((xcd + 8 * lane) / hkv, lqs, lqe, lks, lke);
+        int tl, nbl, Pl, npl;
+        tiling(lqe - lqs, tl, nbl, Pl, npl);
+        items = tl == 0 ? 0 : npl + (tl - 1) * g;
+        lnk = lke - lks;
+      }
+      // the work items of the units ahead of lane l's (more keys, or as many and a lower index)
+      int start = 0;
+      for (int u = 0; u < units; ++u) {
+        const int ku = __builtin_amdgcn_readlane(lnk, u);
+        const int iu = __builtin_amdgcn_readlane(items, u);
+        start += (ku > lnk || (ku == lnk && u < lane)) ? iu : 0;
+      }
+      const unsigned long long hit = __builtin_amdgcn_ballot_w64(lane < units && slot >= start && slot < start + items);
+      if (hit == 0) return;  // past this XCD's work items (the whole workgroup)
+      const int L = (int)__builtin_ctzll(hit);
+      unit = xcd + 8 * L;
+      j = slot - __builtin_amdgcn_readlane(start, L);
+      qs = __builtin_amdgcn_readlane(lqs, L);
+      qe = __builtin_amdgcn_readlane(lqe, L);
+      ks = __builtin_amdgcn_readlane(lks, L);
+      ke = __builtin_amdgcn_readlane(lke, L);
+    } else {
+      const int per_unit = g * num_q_tiles;  // workgroups set aside per unit
+      if (slot >= units * per_unit) return;  // (the whole workgroup)
+      unit = xcd + 8 * (slot / per_unit);
+      j = slot % per_unit;
+      bounds(unit / hkv, qs, qe, ks, ke);
+    }
     b = unit / hkv;
-    // rows of this sequence: nq queries, nk keys (bounds clamped into the buffers)
-    int qs = vl.cu_q[b], qe = vl.cu_q[b + 1], ks = vl.cu_k[b], ke = vl.cu_k[b + 1];
-    qs = min(max(qs, 0), vl.total_q);
-    qe = min(max(qe, qs), min(vl.total_q, qs + n));
-    ks = min(max(ks, 0), vl.total_k);
-    ke = min(max(ke, ks), min(vl.total_k, ks + vl.max_k));
     nq = __builtin_amdgcn_readfirstlane(qe - qs);
     nk = __builtin_amdgcn_readfirstlane(ke - ks);
-    const int tiles = (nq + Cfg::BR - 1) / Cfg::BR;
+    int tiles, nb, P, np;
+    tiling(nq, tiles, nb, P, np);
     if (tiles == 0) return;
-    const int nb = (nq - (tiles - 1) * Cfg::BR + 32 * NB - 1) / (32 * NB);  // row blocks of the last tile
-    const int P = min(g, Cfg::WAVES / nb);  // query heads per workgroup on the last tile
-    const int np = (g + P - 1) / P;         // workgroups of the last tile
     int head;
     if (j < np) {
       qt = tiles - 1;

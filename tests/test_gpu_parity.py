@@ -340,6 +340,20 @@ def test_varlen_clamps_offsets_into_the_tensors(A):
     assert_close(out[:50], ref0, "varlen clamp to max_seqlen_k")
 
 
+@pytest.mark.parametrize("batch", [64, 65])
+def test_varlen_many_sequences(A, batch):
+    """8 KV heads: 64 sequences give each XCD 64 (sequence, KV head) units,
+    taken in order of key count with their work items numbered back to back;
+    65 give 65, taken in index order with the longest sequence's tiles set
+    aside for each.  Key counts repeat (ties in the order); some sequences
+    have no queries or no keys."""
+    g = np.random.default_rng(batch)
+    nq = [int(x) for x in g.integers(0, 300, batch)]
+    nk = [q + int(g.choice([0, 0, 64, 500])) for q in nq]
+    nq[3], nk[7] = 0, 0
+    varlen_case(A, varlen_w(16, 8, 128, True, "bf16"), nq, nk)
+
+
 def test_varlen_speculative_verify_shapes(A):
     """A few queries (1..8 draft tokens) against long caches."""
     varlen_case(A, varlen_w(32, 8, 128, True, "bf16"), [1, 4, 8, 2], [5000, 3000, 4097, 64])
