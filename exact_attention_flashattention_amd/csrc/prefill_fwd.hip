@@ -354,29 +354,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int key0 = window > 0 ? max(0, q0 + off - window + 1) / Cfg::BC * Cfg::BC : 0;
   const int nkt = VARLEN ? max(0, (kend + Cfg::BC - 1) / Cfg::BC - key0 / Cfg::BC)  // tiles to process
                          : (kend + Cfg::BC - 1) / Cfg::BC;
-  // ALiBi slope of this head in raw-score units (the scores are scaled by c = scale·log2 e later)
+  // ALiBi slope of this wave's head in raw-score units (the scores are scaled by c = scale·log2 e later)
   const bool alibi = VARLEN && mk.alibi != nullptr;
   const float alibi_raw = alibi ? mk.alibi[h] * kLog2e / c : 0.f;
-  auto store_rows = [&](auto value_of) ATTN_INLINE {  // O rows of this wave, element (blk, dt, e) -> float
+  if (VARLEN && nkt == 0) {  // no row of this workgroup sees a key: its rows are 0
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
       const int qrow = qw + 32 * blk + l32;
       if (qrow < nq) {
         char* op = o + qo_base + (size_t)qrow * q_stride;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int eh = 0; eh < 4; ++eh) {
-            const int dcol = dt * 32 + 8 * eh + 4 * half;
-            const u32x2 w = {T::pack2(value_of(blk, dt, 4 * eh + 0), value_of(blk, dt, 4 * eh + 1)),
-                             T::pack2(value_of(blk, dt, 4 * eh + 2), value_of(blk, dt, 4 * eh + 3))};
-            gstore8(op + dcol * 2, w);
-          }
+        for (int ch = half; ch < Cfg::CPR; ch += 2) gstore16(op + ch * 16, zero4());
       }
     }
-  };
-  if (VARLEN && nkt == 0) {  // no row of this workgroup sees a key: its rows are 0
-    store_rows([](int, int, int) ATTN_INLINE { return 0.f; });
     return;
   }
 
