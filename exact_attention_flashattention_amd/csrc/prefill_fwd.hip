@@ -70,6 +70,7 @@
 #include "device_common.hpp"
 #include "launchers.hpp"
 
+#include <atomic>
 #include <type_traits>
 
 namespace attn {
@@ -181,8 +182,14 @@ struct MaskArgs {
   const float* alibi;  // [hq] ALiBi slopes, natural-log units per position
 };
 
+// One work item (a query tile of one head, see below) of a workgroup: item
+// `bid`.  `qf` holds the Q operands; with have_q they were read already (by
+// the previous item's prefetch).  next_bid >= 0 (square non-causal kernels
+// only): the workgroup's next item, whose Q operands are read into `qf` once
+// this item's last score MFMA has used them.
 template <class T, int D, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_fwd_kernel(
+__device__ __forceinline__ void prefill_item(
+    const int bid, const int next_bid, u32x4 (&qf)[PrefillCfg<D>::NB][D / 16], const bool have_q,
     const char* __restrict__ q, const char* __restrict__ k, const char* __restrict__ v, char* __restrict__ o,
     int batch, int hq, int hkv, int n, float c, int num_q_tiles, VarlenArgs vl, MaskArgs mk) {
   using Cfg = PrefillCfg<D>;
@@ -193,7 +200,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr uint32_t ROWB = Cfg::ROWB;
   __shared__ __attribute__((aligned(1024))) char lds[Cfg::LDS];
 
-  const int tid = threadIdx.x;
+  // The thread index passes through an opaque move, so that nothing derived
+  // from it is hoisted out of the work-item loop of the persistent kernels
+  // (kept live across the loop, that set-up spills).
+  int tid;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"((int)threadIdx.x));
   const int lane = tid & 63;
   // wave-uniform by construction; readfirstlane lets the compiler keep it (and
   // the LDS-DMA destinations and buffer resources derived from it) in scalar registers
@@ -202,8 +213,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
-  // Work item.  Workgroups are dealt round-robin to the 8 XCDs (blockIdx % 8),
-  // each with its own L2; when the (batch, head) count divides by 8, XCD x is
+  // Work item.  Workgroups are dealt round-robin to the 8 XCDs (blockIdx % 8,
+  // which equals bid % 8 since a persistent grid is a multiple of 8), each
+  // with its own L2; when the (batch, head) count divides by 8, XCD x is
   // given the heads [x·H/8, (x+1)·H/8) so the K/V it streams stay in its L2.
   // Non-causal: an XCD walks its heads one at a time, all query tiles of a
   // head back to back.  Causal: an XCD interleaves its heads and walks query
@@ -235,7 +247,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const uint32_t kv_stride = VARLEN ? (uint32_t)hkv * ROWB : ROWB;
   if constexpr (VARLEN) {
     const int g = hq / hkv;
-    const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+    const int xcd = bid % 8, slot = bid / 8;
     const int units = (batch * hkv - xcd + 7) / 8;  // units of this XCD: xcd, xcd + 8, ...
     // row bounds of sequence bb, clamped into the buffers
     auto bounds = [&](int bb, int& qs_, int& qe_, int& ks_, int& ke_) ATTN_INLINE {
@@ -312,7 +324,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     int bh;
     if (H % 8 == 0) {
       const int per = H / 8;
-      const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+      const int xcd = bid % 8, slot = bid / 8;
       if (CAUSAL) {
         bh = xcd * per + slot % per;
         qt = num_q_tiles - 1 - slot / per;
@@ -321,8 +333,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         qt = slot % num_q_tiles;
       }
     } else {
-      bh = blockIdx.x % H;
-      qt = CAUSAL ? num_q_tiles - 1 - (int)(blockIdx.x / H) : (int)(blockIdx.x / H);
+      bh = bid % H;
+      qt = CAUSAL ? num_q_tiles - 1 - (int)(bid / H) : (int)(bid / H);
     }
     h = bh % hq;
     b = bh / hq;
@@ -339,14 +351,32 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // Q operands (B of Sᵀ = K·Qᵀ): block blk, lane holds query qw + 32·blk + l32,
   // head-dim elements 16·kk + 8·half .. +7
-  u32x4 qf[NB][KK];
+  if (!have_q) {
 #pragma unroll
-  for (int blk = 0; blk < NB; ++blk) {
-    const int qrow = qw + 32 * blk + l32;
-    const char* qp = q + qo_base + (size_t)qrow * q_stride;
+    for (int blk = 0; blk < NB; ++blk) {
+      const int qrow = qw + 32 * blk + l32;
+      const char* qp = q + qo_base + (size_t)qrow * q_stride;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) qf[blk][kk] = qrow < nq ? gload16(qp + (kk * 16 + 8 * half) * 2) : zero4();
+      for (int kk = 0; kk < KK; ++kk) qf[blk][kk] = qrow < nq ? gload16(qp + (kk * 16 + 8 * half) * 2) : zero4();
+    }
   }
+  // Q operands of the workgroup's next item (square non-causal kernels, heads
+  // grouped per XCD as above): read during this item's last vector steps, they
+  // arrive while the item finishes and its output is written.
+  auto prefetch_q = [&]() ATTN_INLINE {
+    const int per = batch * hq / 8;
+    const int slot = next_bid / 8;
+    const int bh2 = (next_bid % 8) * per + slot / num_q_tiles;
+    const int qw2 = (slot % num_q_tiles) * Cfg::BR + wave * 32 * NB;
+    const char* q2 = q + (size_t)bh2 * (size_t)n * ROWB;
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+      const int qrow = qw2 + 32 * blk + l32;
+      const char* qp = q2 + (size_t)qrow * ROWB;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) qf[blk][kk] = qrow < n ? gload16(qp + (kk * 16 + 8 * half) * 2) : zero4();
+    }
+  };
 
   // keys any row of this workgroup can see: [key0, kend), key0 a tile boundary
   const int kend = CAUSAL ? max(0, min(nk, q0 + Cfg::BR + off)) : nk;
@@ -819,7 +849,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     pv_then_load_v(stg, 1);
     pin_matrix_step();
     step_end<false>();
-    // step 4t+3: softmax of 2t+1
+    // step 4t+3: softmax of 2t+1 (the last tile: the next item's Q is read first)
+    if constexpr (LAST && !CAUSAL && !VARLEN) {
+      if (next_bid >= 0) prefetch_q();
+    }
     fetch_half(fetch, std::integral_constant<int, 1>{});
     softmax(key0 + 64 * t + 32);
     pin_vector_step();
@@ -894,6 +927,43 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
+// The square non-causal kernels run persistently: workgroup j takes items j,
+// j + G, j + 2G, ... (G = gridDim.x, a multiple of 8, so every item stays on
+// the XCD the mapping above gives it), reading each next item's Q during the
+// current one.  The other kernels take one item per workgroup.
+template <class T, int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_fwd_kernel(
+    const char* __restrict__ q, const char* __restrict__ k, const char* __restrict__ v, char* __restrict__ o,
+    int batch, int hq, int hkv, int n, float c, int num_q_tiles, VarlenArgs vl, MaskArgs mk, int items) {
+  u32x4 qf[PrefillCfg<D>::NB][D / 16];
+  if constexpr (!CAUSAL && !VARLEN) {
+    bool have_q = false;
+    for (int bid = blockIdx.x; bid < items; bid += (int)gridDim.x) {
+      const int next = bid + (int)gridDim.x < items ? bid + (int)gridDim.x : -1;
+      prefill_item<T, D, CAUSAL, VARLEN>(bid, next, qf, have_q, q, k, v, o, batch, hq, hkv, n, c, num_q_tiles, vl,
+                                         mk);
+      have_q = next >= 0;
+      __syncthreads();  // the output staging in LDS is read before the next item's tiles land there
+    }
+  } else {
+    prefill_item<T, D, CAUSAL, VARLEN>(blockIdx.x, -1, qf, false, q, k, v, o, batch, hq, hkv, n, c, num_q_tiles, vl,
+                                       mk);
+  }
+}
+
+// Compute units of the device `stream` runs on (cached per device; 0 if unknown).
+static int compute_units(hipStream_t stream) {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (stream != nullptr && hipStreamGetDevice(stream, &dev) != hipSuccess) return 0;
+  if (dev < 0 || dev >= 64) return 0;
+  int cus = cached[dev].load(std::memory_order_relaxed);
+  if (cus == 0 && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+    cached[dev].store(cus, std::memory_order_relaxed);
+  return cus > 0 ? cus : 0;
+}
+
 template <class T, int D, bool CAUSAL, bool VARLEN>
 static hipError_t launch_prefill_t(const void* q, const void* k, const void* v, void* o, int batch, int hq, int hkv,
                                    int n, float scale, VarlenArgs vl, MaskArgs mk, hipStream_t stream) {
@@ -901,9 +971,16 @@ static hipError_t launch_prefill_t(const void* q, const void* k, const void* v, 
   const int tiles = (n + Cfg::BR - 1) / Cfg::BR;
   // varlen: 8 XCDs x (units of the fullest XCD) x query heads per unit x tiles
   const long long blocks = VARLEN ? 8LL * ((batch * hkv + 7) / 8) * (hq / hkv) * tiles : (long long)tiles * hq * batch;
-  prefill_fwd_kernel<T, D, CAUSAL, VARLEN><<<dim3((unsigned)blocks), dim3(64 * Cfg::WAVES), 0, stream>>>(
+  // square non-causal kernels with heads grouped per XCD: one persistent
+  // workgroup per compute unit (a workgroup fills a compute unit's LDS and registers)
+  long long grid = blocks;
+  if (!CAUSAL && !VARLEN && (batch * hq) % 8 == 0) {
+    const long long cus = compute_units(stream) / 8 * 8;
+    if (cus > 0 && blocks > cus) grid = cus;
+  }
+  prefill_fwd_kernel<T, D, CAUSAL, VARLEN><<<dim3((unsigned)grid), dim3(64 * Cfg::WAVES), 0, stream>>>(
       static_cast<const char*>(q), static_cast<const char*>(k), static_cast<const char*>(v), static_cast<char*>(o),
-      batch, hq, hkv, n, scale * kLog2e, tiles, vl, mk);
+      batch, hq, hkv, n, scale * kLog2e, tiles, vl, mk, (int)blocks);
   return hipGetLastError();
 }
 
