@@ -658,9 +658,18 @@ __device__ __forceinline__ void prefill_item(
   //            with the row sum itself (two v_dot2 chains, one of them starting
   //            from l); `lim` = -1 forces the raise while the row has no
   //            reference (neg_ref = 0 then).
+  // Where the raise runs: at d=128 inside the vector step, right after the
+  // test; at d=64 after the barrier that ends the vector step, at the start of
+  // the wave's next matrix step and before its first MFMA, so the wave reaches
+  // the barrier without waiting for the test (which hangs on the whole
+  // exponential chain; the phase is the vector step's there).  The raise
+  // touches no LDS and no other wave's data, and the scores it needs are
+  // still in registers.  (At d=128 the longer liveness of the scores spills.)
+  constexpr bool kLateRaise = D == 64;
   constexpr uint32_t kRaiseLimit = (T::kBits256 << 16) | 0xFFFFu;
   constexpr float kRescaleSum = 256.f;
   float neg_ref[NB], lim[NB];
+  float lnew[NB];  // d=128: the row sums with the latest subtile; d=64: its largest probability
 #pragma unroll
   for (int blk = 0; blk < NB; ++blk) {
     neg_ref[blk] = kMatSum ? __builtin_huge_valf() : 0.f;
@@ -689,7 +698,34 @@ __device__ __forceinline__ void prefill_item(
       return ps[0] + ps[1];
     }
   };
-  auto softmax = [&](int s0) ATTN_INLINE {
+  auto raise_ref = [&]() ATTN_INLINE {
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+      float m3[6];
+#pragma unroll
+      for (int i = 0; i < 5; ++i) m3[i] = fmaxf(fmaxf(s[blk][3 * i], s[blk][3 * i + 1]), s[blk][3 * i + 2]);
+      m3[5] = s[blk][15];
+      const float mx = fmaxf(fmaxf(fmaxf(m3[0], m3[1]), m3[2]), fmaxf(fmaxf(m3[3], m3[4]), m3[5]));
+      // the current reference (-inf while the row has none)
+      const float m_old = kMatSum ? (neg_ref[blk] == __builtin_huge_valf() ? kNegInf : -neg_ref[blk])
+                                  : (lim[blk] < 0.f ? kNegInf : -neg_ref[blk]);
+      const float m_new = fmaxf(m_old, max_xor32(mx) * c);
+      const float ref = m_new == kNegInf ? 0.f : m_new;  // a row with no live key stays empty
+      const float alpha = fast_exp2(m_old - ref);
+      lsum[blk][0] *= alpha;
+      l_run[blk] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) oacc[blk][dt] *= alpha;
+      if constexpr (kMatSum) {
+        neg_ref[blk] = m_new == kNegInf ? __builtin_huge_valf() : -ref;
+      } else {
+        neg_ref[blk] = -ref;
+        lim[blk] = m_new == kNegInf ? -1.f : kRescaleSum;
+      }
+      lnew[blk] = probs(blk, -ref, l_run[blk]);
+    }
+  };
+  auto softmax = [&](int s0) ATTN_INLINE -> bool {
     if (s0 + 32 > nk || (CAUSAL && s0 + 31 > qw + off) ||
         (window > 0 && s0 <= qw + 32 * NB - 1 + off - window)) {
 #pragma unroll
@@ -724,7 +760,6 @@ __device__ __forceinline__ void prefill_item(
       }
     }
     bool grow = false;
-    float lnew[NB];
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
       lnew[blk] = probs(blk, neg_ref[blk], l_run[blk]);
@@ -733,36 +768,31 @@ __device__ __forceinline__ void prefill_item(
       else
         grow |= !(lnew[blk] - l_run[blk] <= lim[blk]);  // the subtile's sum
     }
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+    const bool raise = __builtin_amdgcn_ballot_w64(grow) != 0;
+    if constexpr (kLateRaise) return raise;
+    if (raise) raise_ref();
 #pragma unroll
-      for (int blk = 0; blk < NB; ++blk) {
-        float m3[6];
+    for (int blk = 0; blk < NB; ++blk) l_run[blk] = lnew[blk];
+    return false;
+  };
+  // The end of a vector step: its barrier, then (d=64) the raise if the test
+  // asked for one.
+  auto vector_step_end = [&](bool raise) ATTN_INLINE {
+    step_end<true>();
+    if constexpr (kLateRaise) {
+      if (__builtin_expect(raise, 0)) {
+        raise_ref();
+        // the raised state in place of the old (without these pins the
+        // register allocator copies every output accumulator on the common path)
 #pragma unroll
-        for (int i = 0; i < 5; ++i) m3[i] = fmaxf(fmaxf(s[blk][3 * i], s[blk][3 * i + 1]), s[blk][3 * i + 2]);
-        m3[5] = s[blk][15];
-        const float mx = fmaxf(fmaxf(fmaxf(m3[0], m3[1]), m3[2]), fmaxf(fmaxf(m3[3], m3[4]), m3[5]));
-        // the current reference (-inf while the row has none)
-        const float m_old = kMatSum ? (neg_ref[blk] == __builtin_huge_valf() ? kNegInf : -neg_ref[blk])
-                                    : (lim[blk] < 0.f ? kNegInf : -neg_ref[blk]);
-        const float m_new = fmaxf(m_old, max_xor32(mx) * c);
-        const float ref = m_new == kNegInf ? 0.f : m_new;  // a row with no live key stays empty
-        const float alpha = fast_exp2(m_old - ref);
-        lsum[blk][0] *= alpha;
-        l_run[blk] *= alpha;
+        for (int blk = 0; blk < NB; ++blk) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) oacc[blk][dt] *= alpha;
-        if constexpr (kMatSum) {
-          neg_ref[blk] = m_new == kNegInf ? __builtin_huge_valf() : -ref;
-        } else {
-          neg_ref[blk] = -ref;
-          lim[blk] = m_new == kNegInf ? -1.f : kRescaleSum;
+          for (int dt = 0; dt < DT; ++dt) pin(oacc[blk][dt]);
+          pin(lsum[blk]);
+          pin(pf[blk][0]);
+          pin(pf[blk][1]);
         }
-        lnew[blk] = probs(blk, -ref, l_run[blk]);
       }
-    }
-    if constexpr (!kMatSum) {
-#pragma unroll
-      for (int blk = 0; blk < NB; ++blk) l_run[blk] = lnew[blk];
     }
   };
 
@@ -776,6 +806,7 @@ __device__ __forceinline__ void prefill_item(
       pin(neg_ref[blk]);
       if constexpr (!kMatSum) {
         pin(l_run[blk]);
+        pin(lnew[blk]);
         pin(lim[blk]);
       }
     }
@@ -841,9 +872,9 @@ __device__ __forceinline__ void prefill_item(
     const bool fetch = t >= 1 && t + S - 1 < nkt;
     // step 4t+1: softmax of subtile 2t
     fetch_half(fetch, std::integral_constant<int, 0>{});
-    softmax(key0 + 64 * t);
+    const bool raise0 = softmax(key0 + 64 * t);
     pin_vector_step();
-    step_end<true>();
+    vector_step_end(raise0);
     // step 4t+2: scores of 2t+1, P·V of 2t; K of 2t+2, V of 2t+1
     if (LAST) qk(); else qk_load_k(next_stage(stg), 0);
     pv_then_load_v(stg, 1);
@@ -854,9 +885,9 @@ __device__ __forceinline__ void prefill_item(
       if (next_bid >= 0) prefetch_q();
     }
     fetch_half(fetch, std::integral_constant<int, 1>{});
-    softmax(key0 + 64 * t + 32);
+    const bool raise1 = softmax(key0 + 64 * t + 32);
     pin_vector_step();
-    step_end<true>();
+    vector_step_end(raise1);
     // step 4t+4: scores of 2t+2, P·V of 2t+1; K of 2t+3, V of 2t+2; tile t+2 landed
     if (LAST) {
       pv();
