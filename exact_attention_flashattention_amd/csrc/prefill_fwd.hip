@@ -658,14 +658,11 @@ __device__ __forceinline__ void prefill_item(
   //            with the row sum itself (two v_dot2 chains, one of them starting
   //            from l); `lim` = -1 forces the raise while the row has no
   //            reference (neg_ref = 0 then).
-  // Where the raise runs: at d=128 inside the vector step, right after the
-  // test; at d=64 after the barrier that ends the vector step, at the start of
-  // the wave's next matrix step and before its first MFMA, so the wave reaches
-  // the barrier without waiting for the test (which hangs on the whole
-  // exponential chain; the phase is the vector step's there).  The raise
-  // touches no LDS and no other wave's data, and the scores it needs are
-  // still in registers.  (At d=128 the longer liveness of the scores spills.)
-  constexpr bool kLateRaise = D == 64;
+  // The raise runs after the barrier that ends the vector step, at the start
+  // of the wave's next matrix step and before its first MFMA, so the wave
+  // reaches the barrier without waiting for the test (which hangs on the
+  // whole exponential chain).  It touches no LDS and no other wave's data,
+  // and the scores it needs are still in registers.
   constexpr uint32_t kRaiseLimit = (T::kBits256 << 16) | 0xFFFFu;
   constexpr float kRescaleSum = 256.f;
   float neg_ref[NB], lim[NB];
@@ -712,8 +709,8 @@ __device__ __forceinline__ void prefill_item(
       const float m_new = fmaxf(m_old, max_xor32(mx) * c);
       const float ref = m_new == kNegInf ? 0.f : m_new;  // a row with no live key stays empty
       const float alpha = fast_exp2(m_old - ref);
-      lsum[blk][0] *= alpha;
-      l_run[blk] *= alpha;
+      if constexpr (kMatSum) lsum[blk][0] *= alpha;
+      else l_run[blk] *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) oacc[blk][dt] *= alpha;
       if constexpr (kMatSum) {
@@ -768,31 +765,28 @@ __device__ __forceinline__ void prefill_item(
       else
         grow |= !(lnew[blk] - l_run[blk] <= lim[blk]);  // the subtile's sum
     }
-    const bool raise = __builtin_amdgcn_ballot_w64(grow) != 0;
-    if constexpr (kLateRaise) return raise;
-    if (raise) raise_ref();
-#pragma unroll
-    for (int blk = 0; blk < NB; ++blk) l_run[blk] = lnew[blk];
-    return false;
+    return __builtin_amdgcn_ballot_w64(grow) != 0;
   };
-  // The end of a vector step: its barrier, then (d=64) the raise if the test
-  // asked for one.
+  // The end of a vector step: its barrier, then the raise if the test asked
+  // for one, then (d=128) the new row sums take effect.
   auto vector_step_end = [&](bool raise) ATTN_INLINE {
     step_end<true>();
-    if constexpr (kLateRaise) {
-      if (__builtin_expect(raise, 0)) {
-        raise_ref();
-        // the raised state in place of the old (without these pins the
-        // register allocator copies every output accumulator on the common path)
+    if (__builtin_expect(raise, 0)) {
+      raise_ref();
+      // the raised state in place of the old (without these pins the register
+      // allocator copies every output accumulator on the common path)
 #pragma unroll
-        for (int blk = 0; blk < NB; ++blk) {
+      for (int blk = 0; blk < NB; ++blk) {
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) pin(oacc[blk][dt]);
-          pin(lsum[blk]);
-          pin(pf[blk][0]);
-          pin(pf[blk][1]);
-        }
+        for (int dt = 0; dt < DT; ++dt) pin(oacc[blk][dt]);
+        if constexpr (kMatSum) pin(lsum[blk]);
+        pin(pf[blk][0]);
+        pin(pf[blk][1]);
       }
+    }
+    if constexpr (!kMatSum) {
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk) l_run[blk] = lnew[blk];
     }
   };
 
