@@ -329,6 +329,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=8.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the measured MFMA-loop and streaming-read ceilings")
+    ap.add_argument("--device-warmup-s", type=float, default=0.5,
+                    help="seconds of untimed launches of the first region before any timing (clock settling)")
     ap.add_argument("--only", choices=ONLY, default="all", help="run only one region or kernel (profiler runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of the bench, run plain device copies of this many MiB (counter calibration)")
@@ -567,8 +569,21 @@ def main() -> int:
              w.batch * w.hq * S * (w.d + 2) * 4.0, w.name, {"num_splits": S})], finite(out, "4-bit decode")))
     torch.cuda.synchronize()
 
+    # ---- device warm-up, untimed: under sustained load the shader clock takes tens of milliseconds
+    # to settle (per-workgroup time stamps: a launch a few milliseconds into the run took 1.16x as
+    # long as one 25 ms in), so the first region would otherwise be timed partly before it has
+    regions = step_regions + other_regions
+    if args.device_warmup_s > 0 and regions:
+        t0, i = time.perf_counter(), 0
+        while time.perf_counter() - t0 < args.device_warmup_s:
+            for _ in range(8):
+                regions[0].launch(i, None)
+                i += 1
+            torch.cuda.synchronize()
+        log(f"device warm-up: {i} untimed launches of {regions[0].name} in {time.perf_counter() - t0:.2f} s")
+
     # ---- timing
-    for reg in step_regions + other_regions:
+    for reg in regions:
         log(f"region {reg.name}: {W} warm-up, {K} wall-clocked, {max(K, MIN_EVENT_LAUNCHES)} event-timed")
         run_region(torch, stream, reg, K, W)
 
