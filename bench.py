@@ -330,7 +330,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the measured MFMA-loop and streaming-read ceilings")
     ap.add_argument("--device-warmup-s", type=float, default=0.5,
-                    help="seconds of untimed launches of the first region before any timing (clock settling)")
+                    help="seconds of untimed matrix-core loop launches before any timing (clock settling)")
     ap.add_argument("--only", choices=ONLY, default="all", help="run only one region or kernel (profiler runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of the bench, run plain device copies of this many MiB (counter calibration)")
@@ -570,17 +570,21 @@ def main() -> int:
     torch.cuda.synchronize()
 
     # ---- device warm-up, untimed: under sustained load the shader clock takes tens of milliseconds
-    # to settle (per-workgroup time stamps: a launch a few milliseconds into the run took 1.16x as
-    # long as one 25 ms in), so the first region would otherwise be timed partly before it has
+    # to settle (per-workgroup time stamps: a prefill launch a few milliseconds into the run took 1.16x
+    # as long as one 25 ms in), so the first region would otherwise be timed partly before it has.
+    # The library's matrix-core loop serves (a kernel of its own, so no timed kernel's count changes).
     regions = step_regions + other_regions
     if args.device_warmup_s > 0 and regions:
+        lib = A._lib.load()
+        wout = torch.empty(512 * 256, dtype=torch.float32, device=dev)
         t0, i = time.perf_counter(), 0
         while time.perf_counter() - t0 < args.device_warmup_s:
             for _ in range(8):
-                regions[0].launch(i, None)
+                A._lib.check("attn_calib_mfma_bf16", lib.attn_calib_mfma_bf16(wout.data_ptr(), 512, 1024,
+                                                                               stream.cuda_stream))
                 i += 1
             torch.cuda.synchronize()
-        log(f"device warm-up: {i} untimed launches of {regions[0].name} in {time.perf_counter() - t0:.2f} s")
+        log(f"device warm-up: {i} matrix-core loop launches in {time.perf_counter() - t0:.2f} s")
 
     # ---- timing
     for reg in regions:
