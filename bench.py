@@ -280,13 +280,23 @@ class Region:
     def __init__(self, name, launch, kernels, check=None):
         self.name, self.launch, self.kernels, self.check = name, launch, kernels, check
         self.wall_s = 0.0
+        self.warm_launches = 0
         self.ms = []  # per kernel: list of event-timed launch durations
 
 
-def run_region(torch, stream, reg: Region, K: int, W: int) -> None:
-    for i in range(W):
+def run_region(torch, stream, reg: Region, K: int, W: int, warm_s: float = 0.0) -> None:
+    # Untimed warm-up: W launches, continued until warm_s seconds have passed.  The shader clock
+    # follows the load with a lag of milliseconds: after an idle moment, or after a kernel of a
+    # different power draw, a prefill launch took up to 1.35x its settled time, recovering over
+    # some 30 launches (per-dispatch kernel trace, per-workgroup time stamps).
+    t0, i = time.perf_counter(), 0
+    while i < W or time.perf_counter() - t0 < warm_s:
         reg.launch(i, None)
+        i += 1
+        if i % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+    reg.warm_launches = i
     t0 = time.perf_counter()
     for i in range(K):
         reg.launch(i, None)
@@ -329,8 +339,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=8.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the measured MFMA-loop and streaming-read ceilings")
-    ap.add_argument("--device-warmup-s", type=float, default=0.5,
-                    help="seconds of untimed matrix-core loop launches before any timing (clock settling)")
+    ap.add_argument("--region-warmup-s", type=float, default=0.2,
+                    help="each region's untimed warm-up lasts at least W launches and at least this many seconds")
     ap.add_argument("--only", choices=ONLY, default="all", help="run only one region or kernel (profiler runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of the bench, run plain device copies of this many MiB (counter calibration)")
@@ -569,27 +579,13 @@ def main() -> int:
              w.batch * w.hq * S * (w.d + 2) * 4.0, w.name, {"num_splits": S})], finite(out, "4-bit decode")))
     torch.cuda.synchronize()
 
-    # ---- device warm-up, untimed: under sustained load the shader clock takes tens of milliseconds
-    # to settle (per-workgroup time stamps: a prefill launch a few milliseconds into the run took 1.16x
-    # as long as one 25 ms in), so the first region would otherwise be timed partly before it has.
-    # The library's matrix-core loop serves (a kernel of its own, so no timed kernel's count changes).
     regions = step_regions + other_regions
-    if args.device_warmup_s > 0 and regions:
-        lib = A._lib.load()
-        wout = torch.empty(512 * 256, dtype=torch.float32, device=dev)
-        t0, i = time.perf_counter(), 0
-        while time.perf_counter() - t0 < args.device_warmup_s:
-            for _ in range(8):
-                A._lib.check("attn_calib_mfma_bf16", lib.attn_calib_mfma_bf16(wout.data_ptr(), 512, 1024,
-                                                                               stream.cuda_stream))
-                i += 1
-            torch.cuda.synchronize()
-        log(f"device warm-up: {i} matrix-core loop launches in {time.perf_counter() - t0:.2f} s")
 
     # ---- timing
     for reg in regions:
-        log(f"region {reg.name}: {W} warm-up, {K} wall-clocked, {max(K, MIN_EVENT_LAUNCHES)} event-timed")
-        run_region(torch, stream, reg, K, W)
+        run_region(torch, stream, reg, K, W, args.region_warmup_s)
+        log(f"region {reg.name}: {reg.warm_launches} warm-up (at least {W} and {args.region_warmup_s} s), "
+            f"{K} wall-clocked, {max(K, MIN_EVENT_LAUNCHES)} event-timed")
 
     kernels = []
     for reg in step_regions:
