@@ -769,7 +769,7 @@ def write_traffic(base: str) -> int:
                     "matches source_sha.")
     out["command"] = ("cd /tmp && timeout -s KILL 90 rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE --output-format csv "
                       "-d <dir>/<region>_fetch|_write -o run -- python <repo>/bench.py --no-cpu-baseline "
-                      "--only <region> --steps 2 --warmup 1 (calibration: -d <dir>/copy_fetch|copy_write ... "
+                      "--region-warmup-s 0 --only <region> --steps 2 --warmup 1 (calibration: -d <dir>/copy_fetch|copy_write ... "
                       "--copy-calibration-mib 1024 --steps 3); then python bench.py --write-traffic <dir>")
     out["calibration"] = {"copy_bytes": 1 << 30, "fetch_size_kib": cf, "write_size_kib": cw, "fetch_factor": ff,
                           "write_factor": fw}
