@@ -13,8 +13,10 @@
 //   * Two wave groups run anti-phased.  Every wave alternates a matrix step
 //     (score MFMAs of one 32-key subtile, P·V MFMAs of the previous one, and
 //     between them the LDS reads of the K and V operands of the next matrix
-//     step) and a vector step (mask, row max, exponentials and packing of a
-//     subtile, and the tile transfers).  Group 1 runs one step behind group 0
+//     step) and a vector step (mask, exponentials, packing and the raise test
+//     of a subtile, and the tile transfers; the rare raise itself -- row max
+//     and rescale -- runs after the step's barrier).  Group 1 runs one step
+//     behind group 0
 //     and every step ends at a workgroup barrier, so on each SIMD one wave
 //     keeps the matrix core busy while its partner does the softmax
 //     arithmetic -- the two units overlap instead of taking turns.  The
