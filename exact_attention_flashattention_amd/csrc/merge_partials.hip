@@ -12,12 +12,14 @@
 // output columns of one split group, and the split groups take the splits
 // round-robin, so every split's o row is read with contiguous 16-byte loads,
 // several in flight per thread.  Each split group folds its splits against
-// its own maximum in registers, then the groups are merged through LDS with
-// the same rule -- one round trip to memory.  A workgroup covers COLS output
-// columns: all D when there are many rows, 32 when few rows would leave most
-// of the GPU idle.  Reads S·(D+2) floats per row once; with few rows it is
-// bound by memory latency, so each split group folds its splits with a
-// running maximum, which keeps all of a thread's loads independent.
+// its own maximum in registers, then the groups are merged in LDS by the
+// same rule (in a fixed pairwise tree when there are many groups) -- one
+// round trip to memory.  A workgroup covers COLS output columns: all D when there are
+// many rows, 32 or 16 when few rows would leave most of the GPU idle (16 for
+// many splits, so each thread reads at most a few of them).  Reads
+// S·(D+2) floats per row once; with few rows it is bound by memory latency,
+// so each split group folds its splits with a running maximum, which keeps
+// all of a thread's loads independent.
 #include "device_common.hpp"
 #include "launchers.hpp"
 
@@ -49,7 +51,7 @@ __global__ __launch_bounds__(256) void merge_partials_kernel(const float* __rest
   float mg = kNegInf;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float lsum = 0.f;
-#pragma unroll 4
+#pragma unroll 8
   for (int s = g; s < num_splits; s += GROUPS) {
     const float ms = m_[s];
     const float ls = l_[s];
@@ -64,40 +66,80 @@ __global__ __launch_bounds__(256) void merge_partials_kernel(const float* __rest
     acc += w * os;
     lsum += w * ls;
   }
-  acc_s[g][c] = acc;
-  if (c == 0) {
-    l_s[g] = lsum;
-    m_s[g] = mg;
-  }
-  __syncthreads();
 
-  // 2. merge the groups and normalise (empty groups have m = -inf, weight 0)
-  if (tid < QUADS) {
-    float M = m_s[0];
-    for (int r = 1; r < GROUPS; ++r) M = fmaxf(M, m_s[r]);
-    f32x4 tot = {0.f, 0.f, 0.f, 0.f};
-    float l = 0.f;
-    if (M != kNegInf) {
-      for (int r = 0; r < GROUPS; ++r) {
-        const float w = (m_s[r] == kNegInf) ? 0.f : fast_exp2((m_s[r] - M) * kLog2e);
-        tot += w * acc_s[r][tid];
-        l += w * l_s[r];
+  // 2. merge the groups.  Many groups (few rows): pairwise in a fixed tree --
+  // at each level the upper half of the live groups publishes its state and
+  // group g takes in group g + half (every thread of a group holds the
+  // group's m and l); a level's reads and the next level's writes touch
+  // disjoint slots, so one barrier per level.  Few groups: all publish, and
+  // group 0 weighs them against their common maximum.  Empty states have
+  // m = -inf and weight 0.
+  auto take_in = [&](float mo, float lo, f32x4 ao) {
+    const float M = fmaxf(mg, mo);
+    const float wa = (mg == kNegInf) ? 0.f : fast_exp2((mg - M) * kLog2e);
+    const float wb = (mo == kNegInf) ? 0.f : fast_exp2((mo - M) * kLog2e);
+    acc = acc * wa + ao * wb;
+    lsum = lsum * wa + lo * wb;
+    mg = M;
+  };
+  if constexpr (GROUPS >= 32) {
+#pragma unroll
+    for (int half = GROUPS / 2; half >= 1; half /= 2) {
+      if (g >= half && g < 2 * half) {
+        acc_s[g][c] = acc;
+        if (c == 0) {
+          l_s[g] = lsum;
+          m_s[g] = mg;
+        }
+      }
+      __syncthreads();
+      if (g < half) take_in(m_s[g + half], l_s[g + half], acc_s[g + half][c]);
+    }
+  } else {
+    acc_s[g][c] = acc;
+    if (c == 0) {
+      l_s[g] = lsum;
+      m_s[g] = mg;
+    }
+    __syncthreads();
+    if (g == 0) {
+      float M = m_s[0];
+      for (int r = 1; r < GROUPS; ++r) M = fmaxf(M, m_s[r]);
+      acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      lsum = 0.f;
+      if (M != kNegInf) {
+        for (int r = 0; r < GROUPS; ++r) {
+          const float w = (m_s[r] == kNegInf) ? 0.f : fast_exp2((m_s[r] - M) * kLog2e);
+          acc += w * acc_s[r][c];
+          lsum += w * l_s[r];
+        }
       }
     }
-    const float inv = (l > 0.f) ? 1.f / l : 0.f;
-    tot *= inv;
-    u32x2 packed = {T::pack2(tot[0], tot[1]), T::pack2(tot[2], tot[3])};
-    gstore8(reinterpret_cast<char*>(out) + (row * D + col0 + 4 * tid) * 2, packed);
+  }
+
+  // 3. normalise (a row with no keys has l = 0 and is written as 0)
+  if (g == 0) {
+    const float inv = (lsum > 0.f) ? 1.f / lsum : 0.f;
+    acc *= inv;
+    u32x2 packed = {T::pack2(acc[0], acc[1]), T::pack2(acc[2], acc[3])};
+    gstore8(reinterpret_cast<char*>(out) + (row * D + col0 + 4 * c) * 2, packed);
   }
 }
 
-// Rows below this count are spread over D/32 workgroups each.
+// Rows below this count are spread over D/32 (or, with many splits, D/16)
+// workgroups each.
 constexpr int kMergeFewRows = 512;
+
+// With few rows and at least this many splits, workgroups of 16 columns.
+constexpr int kMergeManySplits = 128;
 
 template <class T, int D>
 static hipError_t launch_merge_t(const float* pm, const float* pl, const float* po, int rows, int num_splits,
                                  void* out, hipStream_t stream) {
-  if (rows < kMergeFewRows)
+  if (rows < kMergeFewRows && num_splits >= kMergeManySplits)
+    merge_partials_kernel<T, D, 16><<<dim3((unsigned)rows * (D / 16)), dim3(256), 0, stream>>>(pm, pl, po,
+                                                                                          num_splits, out);
+  else if (rows < kMergeFewRows)
     merge_partials_kernel<T, D, 32><<<dim3((unsigned)rows * (D / 32)), dim3(256), 0, stream>>>(pm, pl, po,
                                                                                           num_splits, out);
   else
