@@ -793,12 +793,15 @@ def test_kv_quantize_then_fused_decode(A):
 
 # --- merge -----------------------------------------------------------------------------
 
-@pytest.mark.parametrize("S", [1, 2, 9, 300])
+# Few rows (15): 32-column workgroups with a pairwise tree over 32 split
+# groups, and from 128 splits on 16-column workgroups over 64 groups; many
+# rows (512, the threshold): whole rows, 8 or 16 groups folded at once.
+@pytest.mark.parametrize("S,B,H", [(1, 3, 5), (2, 3, 5), (9, 3, 5), (127, 3, 5), (128, 3, 5), (300, 3, 5),
+                                   (9, 4, 128), (130, 4, 128)])
 @pytest.mark.parametrize("d,dtype", [(128, torch.bfloat16), (64, torch.float16)])
-def test_merge_random_partials(A, S, d, dtype):
-    announce(f"merge S={S} d={d} {dtype}")
-    gen = torch.Generator().manual_seed(S * 1000 + d)
-    B, H = 3, 5
+def test_merge_random_partials(A, S, B, H, d, dtype):
+    announce(f"merge S={S} B={B} H={H} d={d} {dtype}")
+    gen = torch.Generator().manual_seed(S * 1000 + d + B * H)
     m = torch.rand(B, H, S, generator=gen) * 40 - 5
     l = torch.rand(B, H, S, generator=gen) * 50 + 1
     o = torch.randn(B, H, S, d, generator=gen) * l[..., None]
