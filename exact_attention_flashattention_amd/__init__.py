@@ -15,9 +15,11 @@ Entry points (same names as the C ABI):
   ``attn_decode_splitk_paged``
 * ``decode_splitk_q4(q, k_codes, k_scales, v_codes, v_scales, kv_lens, rotated, num_splits, scale)`` --
   ``attn_decode_splitk_q4``
+* ``decode_splitk_q4_paged(q, k_codes, k_scales, v_codes, v_scales, block_table, kv_lens, rotated, num_splits,
+  scale)`` -- ``attn_decode_splitk_q4_paged``
 * ``kv_quantize_q4(x, rotated, out_rows, codes, scales)`` -- ``attn_kv_quantize_q4``
 * ``merge_partials(part_m, part_l, part_o, out_dtype)`` -- ``attn_merge_partials``
-* ``decode(...)``, ``decode_paged(...)``, ``decode_q4(...)`` -- split-K then merge, back to back on one stream
+* ``decode(...)``, ``decode_paged(...)``, ``decode_q4(...)``, ``decode_q4_paged(...)`` -- split-K then merge, back to back on one stream
 * ``decode_noalloc(q, k_cache, v_cache, kv_lens, num_splits, scale)`` -- ``attn_decode_noalloc``: the same
   split-K and merge with the partial states in the library's fixed scratch array (no workspace)
 * ``decode_num_splits``, ``decode_q4_num_splits``, ``decode_chunk_len``, ``decode_workspace_bytes`` -- host helpers
@@ -34,7 +36,7 @@ from . import _lib
 from ._lib import ATTN_BF16, ATTN_F16, AttnError  # noqa: F401
 
 __all__ = ["prefill_fwd", "prefill_varlen_fwd", "decode_splitk", "decode_splitk_paged", "decode_splitk_q4", "decode_q4",
-           "kv_quantize_q4", "merge_partials", "decode", "decode_paged", "decode_noalloc",
+           "decode_splitk_q4_paged", "decode_q4_paged", "kv_quantize_q4", "merge_partials", "decode", "decode_paged", "decode_noalloc",
            "decode_num_splits", "decode_q4_num_splits", "decode_chunk_len", "decode_workspace_bytes", "AttnError"]
 
 _DTYPES = {torch.bfloat16: ATTN_BF16, torch.float16: ATTN_F16}
@@ -251,6 +253,40 @@ def decode_splitk_q4(q: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Ten
     return pm, pl, po
 
 
+def decode_splitk_q4_paged(q: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Tensor, v_codes: torch.Tensor,
+                           v_scales: torch.Tensor, block_table: torch.Tensor, kv_lens: torch.Tensor, rotated: bool,
+                           num_splits: Optional[int] = None, scale: Optional[float] = None, partials=None):
+    """Partial states over a paged 4-bit cache: ``k_codes, v_codes: [P, Hkv, page, d/2]`` uint8,
+    ``k_scales, v_scales: [P, Hkv, page]`` fp32, ``block_table: [B, max_pages]`` int32 (device).  Same outputs
+    as ``decode_splitk_q4`` over the cache the pages hold."""
+    lib = _lib_handle()
+    if q.dim() != 3 or k_codes.dim() != 4 or v_codes.shape != k_codes.shape or block_table.dim() != 2:
+        raise ValueError("expected q [B, Hq, d], code pools [P, Hkv, page, d/2] and block_table [B, max_pages]")
+    B, hq, d = q.shape
+    P, hkv, page, half = k_codes.shape
+    if 2 * half != d or k_codes.dtype != torch.uint8 or v_codes.dtype != torch.uint8:
+        raise ValueError("code pools must be uint8 [P, Hkv, page, d/2]")
+    for name, t in (("k_scales", k_scales), ("v_scales", v_scales)):
+        if t.shape != (P, hkv, page) or t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32 [P, Hkv, page]")
+    if block_table.dtype != torch.int32 or block_table.shape[0] != B or block_table.device != q.device:
+        raise ValueError("block_table must be an int32 device tensor [B, max_pages]")
+    if kv_lens.dtype != torch.int32 or kv_lens.numel() != B or kv_lens.device != q.device:
+        raise ValueError("kv_lens must be an int32 device tensor with one entry per sequence")
+    _same_device(q, k_codes=k_codes, v_codes=v_codes, k_scales=k_scales, v_scales=v_scales)
+    max_pages = block_table.shape[1]
+    S = decode_q4_num_splits(B, hkv, max_pages * page) if num_splits is None else int(num_splits)
+    pm, pl, po = _partials(partials, B, hq, S, d, q.device)
+    st = lib.attn_decode_splitk_q4_paged(_dev(q, "q"), _dev(k_codes, "k_codes"), _dev(k_scales, "k_scales"),
+                                         _dev(v_codes, "v_codes"), _dev(v_scales, "v_scales"),
+                                         _dev(block_table, "block_table"), max_pages, P, page,
+                                         _dev(kv_lens, "kv_lens"), _dtype_code(q), B, hq, hkv, d, _scale(scale, d),
+                                         int(bool(rotated)), S, _dev(pm, "part_m"), _dev(pl, "part_l"),
+                                         _dev(po, "part_o"), _stream(q))
+    _lib.check("attn_decode_splitk_q4_paged", st)
+    return pm, pl, po
+
+
 def kv_quantize_q4(x: torch.Tensor, rotated: bool, out_rows: Optional[torch.Tensor] = None,
                    codes: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None):
     """Encode rows ``x [..., d]`` (bf16/fp16, device) into 4-bit cache rows: returns ``(codes, scales)``,
@@ -353,4 +389,13 @@ def decode_q4(q: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Tensor, v_
     """Single-query decode over a 4-bit cache: fused-dequant split-K partials then their merge."""
     pm, pl, po = decode_splitk_q4(q, k_codes, k_scales, v_codes, v_scales, kv_lens, rotated, num_splits, scale,
                                   partials)
+    return merge_partials(pm, pl, po, q.dtype)
+
+
+def decode_q4_paged(q: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Tensor, v_codes: torch.Tensor,
+                    v_scales: torch.Tensor, block_table: torch.Tensor, kv_lens: torch.Tensor, rotated: bool,
+                    num_splits: Optional[int] = None, scale: Optional[float] = None, partials=None) -> torch.Tensor:
+    """Single-query decode over a paged 4-bit cache: fused-dequant paged split-K partials then their merge."""
+    pm, pl, po = decode_splitk_q4_paged(q, k_codes, k_scales, v_codes, v_scales, block_table, kv_lens, rotated,
+                                        num_splits, scale, partials)
     return merge_partials(pm, pl, po, q.dtype)

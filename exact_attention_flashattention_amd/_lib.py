@@ -51,6 +51,9 @@ SIGNATURES = {
                                           _vp]),
     "attn_decode_splitk_q4": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                                        _c_int, _c_float, _c_int, _c_int, _vp, _vp, _vp, _vp]),
+    "attn_decode_splitk_q4_paged": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _c_int,
+                                             _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _c_int, _vp, _vp,
+                                             _vp, _vp]),
     "attn_kv_quantize_q4": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _c_int, _vp, _vp, _vp]),
     "attn_decode_noalloc": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float,
                                      _c_int, _vp, _vp]),

@@ -259,6 +259,38 @@ attn_status attn_decode_splitk_q4(const void* q, const void* k_codes, const floa
                                                 chunk, part_m, part_l, part_o, static_cast<hipStream_t>(stream)));
 }
 
+attn_status attn_decode_splitk_q4_paged(const void* q, const void* k_codes, const float* k_scales,
+                                        const void* v_codes, const float* v_scales, const int* block_table,
+                                        int max_pages_per_seq, int num_pages, int page_size, const int* kv_lens,
+                                        int dtype, int batch, int hq, int hkv, int d, float scale, int rotated,
+                                        int num_splits, float* part_m, float* part_l, float* part_o, void* stream) {
+  if (!q || !k_codes || !k_scales || !v_codes || !v_scales || !block_table || !kv_lens || !part_m || !part_l ||
+      !part_o)
+    return ATTN_ERR_NULL_PTR;
+  if (batch < 1 || hq < 1 || hkv < 1 || max_pages_per_seq < 1 || num_pages < 1 || num_splits < 1 ||
+      hq % hkv != 0 || !scale_ok(scale))
+    return ATTN_ERR_BAD_SHAPE;
+  if (page_size < 16 || (page_size & (page_size - 1)) != 0) return ATTN_ERR_UNSUPPORTED;
+  if ((d != 64 && d != 128) || !dtype_ok(dtype)) return ATTN_ERR_UNSUPPORTED;
+  const long long max_kv_len = (long long)max_pages_per_seq * page_size;
+  const int groups = (hq / hkv + 15) / 16;
+  if (max_kv_len * d >= (1LL << 31) || (long long)num_pages * hkv * page_size * d >= kMaxElems ||
+      (long long)batch * max_pages_per_seq >= (1LL << 31) || batch > 65535 || (long long)hkv * groups > 65535 ||
+      num_splits > 65535 || (long long)batch * hq * num_splits * d >= kMaxElems)
+    return ATTN_ERR_TOO_LARGE;
+  if (!aligned16(q) || !aligned16(k_codes) || !aligned16(v_codes) || !aligned16(k_scales) || !aligned16(v_scales) ||
+      !aligned16(part_o))
+    return ATTN_ERR_MISALIGNED;
+  int shift = 0;
+  while ((1 << shift) < page_size) ++shift;
+  const int chunk = attn_decode_chunk_len((int)max_kv_len, num_splits);
+  return from_hip(attn::launch_decode_splitk_q4_paged(q, k_codes, k_scales, v_codes, v_scales, block_table,
+                                                      max_pages_per_seq, num_pages, shift, kv_lens,
+                                                      dtype == ATTN_BF16, batch, hq, hkv, d, scale, rotated != 0,
+                                                      num_splits, chunk, part_m, part_l, part_o,
+                                                      static_cast<hipStream_t>(stream)));
+}
+
 attn_status attn_kv_quantize_q4(const void* x, int rows, int d, int dtype, int rotated, const int* out_rows,
                                 int out_capacity, void* codes, float* scales, void* stream) {
   if (!x || !codes || !scales) return ATTN_ERR_NULL_PTR;

@@ -30,6 +30,17 @@
 // (8-byte) load.  V is dequantised into wave-private LDS in natural order and
 // read back with the transpose read as in the 16-bit kernel.
 //
+// Paged caches (PAGED = true; "PagedAttention's kernel difference" in
+// section 5 of "Attention Computation in Practice"): the codes live in a pool
+// [num_pages, Hkv, P, d/2] and the scales in [num_pages, Hkv, P]; logical row
+// j of sequence b is row j % P of page block_table[b][j / P].  P is a power
+// of two >= 16 and splits start on multiples of 64, so each 16-row half of a
+// 32-key step lies in one page and gathers through its own buffer resources.
+// The V codes are then loaded per half (lane l: row 16·half + l/4, a quarter
+// of it) instead of two lanes per row across the step; they land in LDS in
+// the same natural order.  The page ids of the split's next 64 pages sit one
+// per lane in a VGPR and are picked out with v_readlane.
+//
 // The P·V product runs in bf16 whatever the query's type: its B operand is a
 // probability (up to 2^8 before the reference is raised) times the V row's
 // scale, which for legal fp16 V rows (|v| up to 65504, scale up to ~1.1e4)
@@ -117,7 +128,7 @@ struct Q4Stage {
 
 }  // namespace
 
-template <class T, int D>
+template <class T, int D, bool PAGED>
 // Two waves per SIMD (the register budget of each is 256): the 4-bit steps are
 // small, and a second wave per SIMD hides the memory latency that one wave,
 // even with four steps in flight, leaves exposed (measured: 79 -> 58 us on a
@@ -126,7 +137,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const char* __restrict__ q, const char* __restrict__ kc, const float* __restrict__ ks,
     const char* __restrict__ vc, const float* __restrict__ vs, const int* __restrict__ kv_lens, int max_kv_len,
     int hq, int hkv, int g, int chunk, int num_splits, float c, int rotated, float* __restrict__ part_m,
-    float* __restrict__ part_l, float* __restrict__ part_o) {
+    float* __restrict__ part_l, float* __restrict__ part_o, const int* __restrict__ table, int max_pages,
+    int num_pages, int page_shift) {
   constexpr int KK = D / 32;             // 16x16x32 k-steps over the head dimension
   constexpr int DG = D / 4;              // dimensions per lane group
   constexpr int DT = D / 16;             // 16-row output tiles of the head dimension
@@ -237,8 +249,57 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const uint32_t s_off = (uint32_t)(4 * grp) * 4;                       // + 64·sb for half sb
   const int vrow = lane / (64 / 32);                                    // V rows: two lanes per row
   const uint32_t v_off = (uint32_t)vrow * RB + (lane & 1) * (RB / 2);   // VB = RB/2 bytes per lane
+  // paged: V loaded per 16-row half, lane l taking row l/4 of the half, quarter l%4 of it
+  const uint32_t pv_off = (uint32_t)(lane >> 2) * RB + (lane & 3) * (RB / 4);
+
+  // paged: ids of pages [tab_base, tab_base + 64) of this sequence, lane i
+  // holding page tab_base + i (entries past the table row read as 0)
+  int tab = 0, tab_base = 0;
+  auto fetch_table = [&](int p0) {
+    tab_base = p0;
+    const int p = p0 + lane;
+    tab = p < max_pages ? table[(size_t)b * max_pages + p] : 0;
+  };
+  if constexpr (PAGED) fetch_table(start >> page_shift);
+  // pool row of logical row `key` (a multiple of 16) of KV head kh
+  auto paged_row = [&](int key) -> size_t {
+    const int p = key >> page_shift;
+    if (p - tab_base >= 64) fetch_table(p);
+    int id = __builtin_amdgcn_readlane(tab, p - tab_base);
+    id = id < 0 ? 0 : (id >= num_pages ? num_pages - 1 : id);
+    return (((size_t)id * hkv + kh) << page_shift) + (key & ((1 << page_shift) - 1));
+  };
 
   auto load = [&](Q4Stage<D>& st, int k0) {
+    if constexpr (PAGED) {
+      bufres rk[2], rv[2], rks[2], rvs[2];
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        const int kr = k0 + 16 * sb;
+        // (readfirstlane: a resource in vector registers would make every load a waterfall loop)
+        const int rows = __builtin_amdgcn_readfirstlane(end - kr < 0 ? 0 : (end - kr > 16 ? 16 : end - kr));
+        const size_t row = rows > 0 ? paged_row(kr) : 0;  // past the end: reads nothing
+        rk[sb] = make_bufres(kc + row * RB, (uint32_t)rows * RB);
+        rv[sb] = make_bufres(vc + row * RB, (uint32_t)rows * RB);
+        rks[sb] = make_bufres(ks + row, (uint32_t)rows * 4);
+        rvs[sb] = make_bufres(vs + row, (uint32_t)rows * 4);
+      }
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        if constexpr (D == 128) {
+          st.k[sb][0] = bload16(rk[sb], k_off);
+          st.v[sb] = bload16(rv[sb], pv_off);
+        } else {
+          st.k8[sb] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rk[sb], k_off, 0, 0));
+          const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv[sb], pv_off, 0, 0));
+          st.v[0][2 * sb] = w[0];
+          st.v[0][2 * sb + 1] = w[1];
+        }
+        st.ks[sb] = __builtin_bit_cast(f32x4, bload16(rks[sb], s_off));
+        st.vs[sb] = __builtin_bit_cast(f32x4, bload16(rvs[sb], s_off));
+      }
+      return;
+    }
     const uint32_t rows = k0 < end ? (uint32_t)(end - k0) : 0u;  // past the end: reads nothing
     const bufres rk = make_bufres(kbase + (size_t)k0 * RB, rows * RB);
     const bufres rv = make_bufres(vbase + (size_t)k0 * RB, rows * RB);
@@ -266,17 +327,38 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   auto process = [&](const Q4Stage<D>& st, int k0) {
     __syncthreads();  // previous step's transpose reads are done with the buffer
     // V codes -> 16-bit values in LDS, natural dimension order: this lane's VB bytes
-    // are dimensions (lane & 1)·D/2 .. + D/2 - 1 of row vrow
+    // are dimensions (lane & 1)·D/2 .. + D/2 - 1 of row vrow (paged: per half h,
+    // dimensions (lane & 3)·D/4 .. + D/4 - 1 of row 16·h + lane/4)
+    if constexpr (PAGED) {
 #pragma unroll
-    for (int i = 0; i < VB / 16; ++i) {
-      u32x4 lo, hi;
-      dequant8<Bf16>(u32x2{st.v[i][0], st.v[i][1]}, lo, hi);
-      const uint32_t at = vrow * VP + (lane & 1) * D + i * 64;
-      lds_write16(vlds, at, lo);
-      lds_write16(vlds, at + 16, hi);
-      dequant8<Bf16>(u32x2{st.v[i][2], st.v[i][3]}, lo, hi);
-      lds_write16(vlds, at + 32, lo);
-      lds_write16(vlds, at + 48, hi);
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const uint32_t at = (16 * h2 + (lane >> 2)) * VP + (lane & 3) * (D / 2);
+        u32x4 lo, hi;
+        if constexpr (D == 128) {
+          dequant8<Bf16>(u32x2{st.v[h2][0], st.v[h2][1]}, lo, hi);
+          lds_write16(vlds, at, lo);
+          lds_write16(vlds, at + 16, hi);
+          dequant8<Bf16>(u32x2{st.v[h2][2], st.v[h2][3]}, lo, hi);
+          lds_write16(vlds, at + 32, lo);
+          lds_write16(vlds, at + 48, hi);
+        } else {
+          dequant8<Bf16>(u32x2{st.v[0][2 * h2], st.v[0][2 * h2 + 1]}, lo, hi);
+          lds_write16(vlds, at, lo);
+          lds_write16(vlds, at + 16, hi);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < VB / 16; ++i) {
+        u32x4 lo, hi;
+        dequant8<Bf16>(u32x2{st.v[i][0], st.v[i][1]}, lo, hi);
+        const uint32_t at = vrow * VP + (lane & 1) * D + i * 64;
+        lds_write16(vlds, at, lo);
+        lds_write16(vlds, at + 16, hi);
+        dequant8<Bf16>(u32x2{st.v[i][2], st.v[i][3]}, lo, hi);
+        lds_write16(vlds, at + 32, lo);
+        lds_write16(vlds, at + 48, hi);
+      }
     }
     // scores: s[sb][e] is key k0 + 16·sb + 4·grp + e against query column r
     f32x4 s[2];
@@ -401,33 +483,58 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   }
 }
 
-template <class T, int D>
+template <class T, int D, bool PAGED>
 static hipError_t launch_q4_t(const void* q, const void* kc, const float* ks, const void* vc, const float* vs,
                               const int* kv_lens, int max_kv_len, int batch, int hq, int hkv, float scale, int rotated,
-                              int num_splits, int chunk, float* pm, float* pl, float* po, hipStream_t stream) {
+                              int num_splits, int chunk, float* pm, float* pl, float* po, const int* table,
+                              int max_pages, int num_pages, int page_shift, hipStream_t stream) {
   const int g = hq / hkv;
   const int groups = (g + 15) / 16;
   dim3 grid(num_splits, hkv * groups, batch);
-  decode_q4_kernel<T, D><<<grid, dim3(64), 0, stream>>>(
+  decode_q4_kernel<T, D, PAGED><<<grid, dim3(64), 0, stream>>>(
       static_cast<const char*>(q), static_cast<const char*>(kc), ks, static_cast<const char*>(vc), vs, kv_lens,
-      max_kv_len, hq, hkv, g, chunk, num_splits, scale * kLog2e, rotated, pm, pl, po);
+      max_kv_len, hq, hkv, g, chunk, num_splits, scale * kLog2e, rotated, pm, pl, po, table, max_pages, num_pages,
+      page_shift);
   return hipGetLastError();
+}
+
+template <bool PAGED>
+static hipError_t launch_q4_any(const void* q, const void* kc, const float* ks, const void* vc, const float* vs,
+                                const int* kv_lens, int max_kv_len, bool bf16, int batch, int hq, int hkv, int d,
+                                float scale, bool rotated, int num_splits, int chunk, float* pm, float* pl, float* po,
+                                const int* table, int max_pages, int num_pages, int page_shift, hipStream_t stream) {
+  const int rot = rotated ? 1 : 0;
+  if (bf16)
+    return d == 64 ? launch_q4_t<Bf16, 64, PAGED>(q, kc, ks, vc, vs, kv_lens, max_kv_len, batch, hq, hkv, scale, rot,
+                                                  num_splits, chunk, pm, pl, po, table, max_pages, num_pages,
+                                                  page_shift, stream)
+                   : launch_q4_t<Bf16, 128, PAGED>(q, kc, ks, vc, vs, kv_lens, max_kv_len, batch, hq, hkv, scale, rot,
+                                                   num_splits, chunk, pm, pl, po, table, max_pages, num_pages,
+                                                   page_shift, stream);
+  return d == 64 ? launch_q4_t<F16, 64, PAGED>(q, kc, ks, vc, vs, kv_lens, max_kv_len, batch, hq, hkv, scale, rot,
+                                               num_splits, chunk, pm, pl, po, table, max_pages, num_pages, page_shift,
+                                               stream)
+                 : launch_q4_t<F16, 128, PAGED>(q, kc, ks, vc, vs, kv_lens, max_kv_len, batch, hq, hkv, scale, rot,
+                                                num_splits, chunk, pm, pl, po, table, max_pages, num_pages,
+                                                page_shift, stream);
 }
 
 hipError_t launch_decode_splitk_q4(const void* q, const void* k_codes, const float* k_scales, const void* v_codes,
                                    const float* v_scales, const int* kv_lens, int max_kv_len, bool bf16, int batch,
                                    int hq, int hkv, int d, float scale, bool rotated, int num_splits, int chunk,
                                    float* part_m, float* part_l, float* part_o, hipStream_t stream) {
-  const int rot = rotated ? 1 : 0;
-  if (bf16)
-    return d == 64 ? launch_q4_t<Bf16, 64>(q, k_codes, k_scales, v_codes, v_scales, kv_lens, max_kv_len, batch, hq,
-                                           hkv, scale, rot, num_splits, chunk, part_m, part_l, part_o, stream)
-                   : launch_q4_t<Bf16, 128>(q, k_codes, k_scales, v_codes, v_scales, kv_lens, max_kv_len, batch, hq,
-                                            hkv, scale, rot, num_splits, chunk, part_m, part_l, part_o, stream);
-  return d == 64 ? launch_q4_t<F16, 64>(q, k_codes, k_scales, v_codes, v_scales, kv_lens, max_kv_len, batch, hq,
-                                        hkv, scale, rot, num_splits, chunk, part_m, part_l, part_o, stream)
-                 : launch_q4_t<F16, 128>(q, k_codes, k_scales, v_codes, v_scales, kv_lens, max_kv_len, batch, hq,
-                                         hkv, scale, rot, num_splits, chunk, part_m, part_l, part_o, stream);
+  return launch_q4_any<false>(q, k_codes, k_scales, v_codes, v_scales, kv_lens, max_kv_len, bf16, batch, hq, hkv, d,
+                              scale, rotated, num_splits, chunk, part_m, part_l, part_o, nullptr, 0, 0, 0, stream);
+}
+
+hipError_t launch_decode_splitk_q4_paged(const void* q, const void* k_codes, const float* k_scales,
+                                         const void* v_codes, const float* v_scales, const int* block_table,
+                                         int max_pages, int num_pages, int page_shift, const int* kv_lens, bool bf16,
+                                         int batch, int hq, int hkv, int d, float scale, bool rotated, int num_splits,
+                                         int chunk, float* part_m, float* part_l, float* part_o, hipStream_t stream) {
+  return launch_q4_any<true>(q, k_codes, k_scales, v_codes, v_scales, kv_lens, max_pages << page_shift, bf16, batch,
+                             hq, hkv, d, scale, rotated, num_splits, chunk, part_m, part_l, part_o, block_table,
+                             max_pages, num_pages, page_shift, stream);
 }
 
 }  // namespace attn

@@ -38,6 +38,15 @@ hipError_t launch_decode_splitk_q4(const void* q, const void* k_codes, const flo
                                    int hq, int hkv, int d, float scale, bool rotated, int num_splits, int chunk,
                                    float* part_m, float* part_l, float* part_o, hipStream_t stream);
 
+// The same over paged pools: codes [num_pages, hkv, 1 << page_shift, d/2] and
+// scales [num_pages, hkv, 1 << page_shift]; row j of sequence b is row j % page
+// of page block_table[b * max_pages + j / page].
+hipError_t launch_decode_splitk_q4_paged(const void* q, const void* k_codes, const float* k_scales,
+                                         const void* v_codes, const float* v_scales, const int* block_table,
+                                         int max_pages, int num_pages, int page_shift, const int* kv_lens, bool bf16,
+                                         int batch, int hq, int hkv, int d, float scale, bool rotated, int num_splits,
+                                         int chunk, float* part_m, float* part_l, float* part_o, hipStream_t stream);
+
 // Rows [rows, d] of 16-bit values -> E2M1 codes [.., d/2] and fp32 scales, row i
 // written to row out_rows[i] (or i) of the outputs when inside [0, out_capacity).
 hipError_t launch_quantize_q4(const void* x, int rows, int d, bool bf16, bool rotated, float norm, const int* out_rows,

@@ -259,6 +259,43 @@ attn_status attn_decode_splitk_q4(const void* q, const void* k_codes, const floa
                                   float* part_l, float* part_o, void* stream);
 
 /*
+ * attn_decode_splitk_q4_paged -- attn_decode_splitk_q4 over a paged 4-bit
+ * cache: the page pool and block table of attn_decode_splitk_paged ("PagedAttention's
+ * kernel difference" in section 5 of "Attention Computation in Practice")
+ * holding the codes and row scales of attn_decode_splitk_q4 ("Why a quantised
+ * cache needs a fused kernel" on "Attention from the kernel's side").
+ * Logical cache row j of sequence b is row j % page_size of page
+ * block_table[b·max_pages_per_seq + j / page_size], in both the code pool and
+ * the scale pool.  Partials, splits and units are those of
+ * attn_decode_splitk_q4 with max_kv_len = max_pages_per_seq · page_size; for
+ * the same logical cache contents the partials are bit-identical.
+ *
+ *   q           : [batch, hq, d]                          elements of `dtype`
+ *   k_codes     : [num_pages, hkv, page_size, d/2] bytes (E2M1 pairs as for
+ *                 attn_decode_splitk_q4)
+ *   k_scales    : [num_pages, hkv, page_size] fp32
+ *   v_codes, v_scales : the same for V
+ *   block_table : [batch, max_pages_per_seq] int32, DEVICE memory; only the
+ *                 first ceil(kv_lens[b] / page_size) entries of row b are
+ *                 used; ids outside [0, num_pages) are clamped into it, so no
+ *                 read leaves the pools.  Pages may be shared.
+ *   kv_lens     : [batch] int32, DEVICE memory, clamped into
+ *                 [0, max_pages_per_seq · page_size]
+ *   page_size   : a power of two >= 16 (else ATTN_ERR_UNSUPPORTED)
+ *   rotated, num_splits, part_m, part_l, part_o : as for
+ *                 attn_decode_splitk_q4 (no masking variants)
+ *
+ * Every pointer must be 16-byte aligned.  Limits: max_pages_per_seq ·
+ * page_size below 2^31 / d; num_pages·hkv·page_size·d below 2^40 (else
+ * ATTN_ERR_TOO_LARGE).
+ */
+attn_status attn_decode_splitk_q4_paged(const void* q, const void* k_codes, const float* k_scales,
+                                        const void* v_codes, const float* v_scales, const int* block_table,
+                                        int max_pages_per_seq, int num_pages, int page_size, const int* kv_lens,
+                                        int dtype, int batch, int hq, int hkv, int d, float scale, int rotated,
+                                        int num_splits, float* part_m, float* part_l, float* part_o, void* stream);
+
+/*
  * attn_kv_quantize_q4 -- encode rows of keys or values into the 4-bit cache
  * format read by attn_decode_splitk_q4 (the write side of the fused-dequant
  * cache: rows are quantised once, as they enter the cache).

@@ -18,6 +18,7 @@ from .attention import (  # noqa: F401
     decode,
     decode_paged,
     decode_q4,
+    decode_q4_paged,
     dequantize_e2m1_rows,
     quantize_e2m1_rows,
     e2m1_value,

@@ -376,6 +376,38 @@ def decode_q4(q, k_codes, k_scales, v_codes, v_scales, kv_lens, scale: float, ro
     return decode(q, K, V, kv_lens, scale)
 
 
+def decode_q4_paged(q, k_codes, k_scales, v_codes, v_scales, block_table, kv_lens, scale: float, rotated: bool):
+    """Single-query attention over a paged 4-bit cache.
+
+    Pools ``k_codes, v_codes: [P, Hkv, page_size, d/2]`` uint8 and ``k_scales,
+    v_scales: [P, Hkv, page_size]``; ``block_table: [B, max_pages]``.  Each
+    sequence's code rows and scales are gathered through the same table as in
+    ``gather_pages`` ("PagedAttention's kernel difference", section 5 of
+    "Attention Computation in Practice") and ``decode_q4`` runs on the
+    contiguous cache they form: paging moves rows, dequantisation fixes their
+    values.  Returns ``O: [B, Hq, d]`` in fp64.
+    """
+    k_codes, v_codes = np.asarray(k_codes, dtype=np.uint8), np.asarray(v_codes, dtype=np.uint8)
+    k_scales, v_scales = _f64(k_scales), _f64(v_scales)
+    B = np.asarray(q).shape[0]
+    _, Hkv, ps, half = k_codes.shape
+    capacity = np.asarray(block_table).shape[1] * ps
+    lens = [int(n) for n in kv_lens]
+    for b, n in enumerate(lens):
+        if not 0 <= n <= capacity:
+            raise ValueError(f"kv_lens[{b}]={n} outside [0, {capacity}]")
+    L = max([1] + lens)
+    kc, vc = np.zeros((B, Hkv, L, half), np.uint8), np.zeros((B, Hkv, L, half), np.uint8)
+    ks, vs = np.zeros((B, Hkv, L)), np.zeros((B, Hkv, L))
+    for b, n in enumerate(lens):
+        for kh in range(Hkv):
+            kc[b, kh, :n] = gather_pages(k_codes, block_table[b], n, kh)
+            vc[b, kh, :n] = gather_pages(v_codes, block_table[b], n, kh)
+            ks[b, kh, :n] = gather_pages(k_scales[..., None], block_table[b], n, kh)[:, 0]
+            vs[b, kh, :n] = gather_pages(v_scales[..., None], block_table[b], n, kh)[:, 0]
+    return decode_q4(q, kc, ks, vc, vs, lens, scale, rotated)
+
+
 def _merge_arrays(ma, la, oa, mb, lb, ob):
     """The two-state merge rule, elementwise over any leading shape.
 

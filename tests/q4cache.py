@@ -37,3 +37,41 @@ def q4_inputs(w, rotated: bool, device, salt: int = 0, kv_lens=None, max_kv_len=
     del kc
     vq, vs = encode(vc, rotated, device)
     return q, kq, ks, vq, vs, lens
+
+
+def paged(kq, ks, vq, vs, kv_lens, page_size: int, seed: int, spare_pages: int = 0):
+    """Lay a contiguous 4-bit cache (codes ``[B, Hkv, Lmax, d/2]``, scales
+    ``[B, Hkv, Lmax]``) out as paged pools, as ``workloads.paged_from_cache``
+    does for 16-bit caches: sequence ``b`` takes ``ceil(kv_lens[b] / page)``
+    pages of a seeded random permutation, ``spare_pages`` more belong to nobody.
+    Rows that no cache row was copied to (spare pages, last-page tails) hold
+    code byte 0xFF and a NaN scale.  Returns ``(k_codes, k_scales, v_codes,
+    v_scales, block_table)``: pools ``[P, Hkv, page, d/2]`` / ``[P, Hkv, page]``
+    on the caches' device and an int32 CPU table ``[B, ceil(Lmax / page)]``
+    holding -1 past each sequence's pages.  Only rows are moved."""
+    B, hkv, L, half = kq.shape
+    ps = page_size
+    lens = [int(x) for x in kv_lens.tolist()]
+    need = [-(-n // ps) for n in lens]
+    total = max(1, sum(need) + spare_pages)
+    gen = torch.Generator()
+    gen.manual_seed(seed & ((1 << 63) - 1))
+    perm = torch.randperm(total, generator=gen)
+    table = torch.full((B, -(-L // ps)), -1, dtype=torch.int32)
+    dev = kq.device
+    pools = []
+    for codes, scales in ((kq, ks), (vq, vs)):
+        pc = torch.full((total, hkv, ps, half), 0xFF, dtype=torch.uint8, device=dev)
+        psc = torch.full((total, hkv, ps), float("nan"), dtype=torch.float32, device=dev)
+        pos = 0
+        for b in range(B):
+            for i in range(need[b]):
+                page = int(perm[pos + i])
+                table[b, i] = page
+                lo, hi = i * ps, min((i + 1) * ps, lens[b])
+                pc[page, :, :hi - lo] = codes[b, :, lo:hi]
+                psc[page, :, :hi - lo] = scales[b, :, lo:hi]
+            pos += need[b]
+        pools += [pc, psc]
+    return pools[0], pools[1], pools[2], pools[3], table
+

@@ -130,6 +130,27 @@ def test_decode_q4_rejects_bad_arguments(lib, kw, status):
     assert decode_q4(lib, **kw) == status
 
 
+def decode_q4_paged(lib, q=P, kc=P, ks=P, vc=P, vs=P, table=P, max_pages=8, num_pages=20, ps=16, lens=P, dtype=BF16,
+                    batch=2, hq=4, hkv=2, d=128, scale=0.1, rot=0, S=2, pm=P, pl=P, po=P):
+    return lib.attn_decode_splitk_q4_paged(q, kc, ks, vc, vs, table, max_pages, num_pages, ps, lens, dtype, batch, hq,
+                                           hkv, d, scale, rot, S, pm, pl, po, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), NULL), (dict(kc=None), NULL), (dict(ks=None), NULL), (dict(vc=None), NULL), (dict(vs=None), NULL),
+    (dict(table=None), NULL), (dict(lens=None), NULL), (dict(pm=None), NULL), (dict(pl=None), NULL),
+    (dict(po=None), NULL),
+    (dict(max_pages=0), SHAPE), (dict(num_pages=0), SHAPE), (dict(S=0), SHAPE), (dict(batch=0), SHAPE),
+    (dict(hq=3), SHAPE), (dict(scale=float("nan")), SHAPE),
+    (dict(ps=8), UNSUP), (dict(ps=48), UNSUP), (dict(ps=0), UNSUP), (dict(d=96), UNSUP), (dict(dtype=3), UNSUP),
+    (dict(q=P + 2), MISAL), (dict(kc=P + 8), MISAL), (dict(ks=P + 4), MISAL), (dict(vc=P + 4), MISAL),
+    (dict(vs=P + 8), MISAL), (dict(po=P + 4), MISAL),
+    (dict(max_pages=1 << 20, ps=64), BIG), (dict(num_pages=1 << 30, ps=1024), BIG), (dict(batch=70000), BIG),
+])
+def test_decode_q4_paged_rejects_bad_arguments(lib, kw, status):
+    assert decode_q4_paged(lib, **kw) == status
+
+
 def quant(lib, x=P, rows=10, d=128, dtype=BF16, rot=1, out_rows=None, cap=10, codes=P, scales=P):
     return lib.attn_kv_quantize_q4(x, rows, d, dtype, rot, out_rows, cap, codes, scales, None)
 

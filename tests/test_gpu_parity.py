@@ -700,21 +700,14 @@ def test_decode_q4_fp16_large_values(A, d, rotated):
     q4_case(A, w, torch.tensor([1024, 700, 65], dtype=torch.int32), 1024, 3, None, rotated, v_mult=8192.0)
 
 
-def test_decode_q4_long_context_full(A):
-    """The 262144-key cache encoded as rotated 4-bit rows (by the oracle's encoder on the host), the
-    benchmarked launch, whole output against the oracle on the dequantised rows; the HIP encoder produces
-    the same codes and scales from the same rows bit for bit."""
-    announce(f"q4 {DEC.name}")
+@pytest.fixture(scope="module")
+def q4_full():
+    """The 262144-key cache encoded as rotated 4-bit rows by the oracle's encoder on the host, with the
+    16-bit rows it came from and the oracle's output over the dequantised rows (shared by the contiguous
+    and the paged full-size tests: the host encoding takes about a minute)."""
     q, kc, vc, lens = workloads.decode_inputs(DEC, device=DEV)
     kq, ks = q4cache.encode(kc, True, DEV)
     vq, vs = q4cache.encode(vc, True, DEV)
-    hk, hks = A.kv_quantize_q4(kc, True)
-    hv, hvs = A.kv_quantize_q4(vc, True)
-    torch.cuda.synchronize()
-    assert torch.equal(hk, kq) and torch.equal(hks, ks) and torch.equal(hv, vq) and torch.equal(hvs, vs)
-    del kc, vc, hk, hks, hv, hvs
-    out = A.decode_q4(q, kq, ks, vq, vs, lens.to(DEV), True, None, DEC.scale)
-    torch.cuda.synchronize()
     g = DEC.hq // DEC.hkv
     qf = f64(q)
     ref = np.zeros((1, DEC.hq, DEC.d))
@@ -722,7 +715,92 @@ def test_decode_q4_long_context_full(A):
         K = oracle.dequantize_e2m1_rows(kq[0, kh].cpu().numpy(), ks[0, kh].cpu().double().numpy(), True)
         V = oracle.dequantize_e2m1_rows(vq[0, kh].cpu().numpy(), vs[0, kh].cpu().double().numpy(), True)
         ref[0, kh * g:(kh + 1) * g] = oracle.attention_rows(qf[0, kh * g:(kh + 1) * g], K, V, DEC.scale)
-    assert_close(out, ref, f"q4 {DEC.name}")
+    return dict(q=q, kc=kc, vc=vc, lens=lens, kq=kq, ks=ks, vq=vq, vs=vs, ref=ref)
+
+
+def test_decode_q4_long_context_full(A, q4_full):
+    """The 262144-key cache encoded as rotated 4-bit rows (by the oracle's encoder on the host), the
+    benchmarked launch, whole output against the oracle on the dequantised rows; the HIP encoder produces
+    the same codes and scales from the same rows bit for bit."""
+    announce(f"q4 {DEC.name}")
+    f = q4_full
+    hk, hks = A.kv_quantize_q4(f["kc"], True)
+    hv, hvs = A.kv_quantize_q4(f["vc"], True)
+    torch.cuda.synchronize()
+    assert torch.equal(hk, f["kq"]) and torch.equal(hks, f["ks"]) and torch.equal(hv, f["vq"])
+    assert torch.equal(hvs, f["vs"])
+    del hk, hks, hv, hvs
+    out = A.decode_q4(f["q"], f["kq"], f["ks"], f["vq"], f["vs"], f["lens"].to(DEV), True, None, DEC.scale)
+    torch.cuda.synchronize()
+    assert_close(out, f["ref"], f"q4 {DEC.name}")
+
+
+# --- paged 4-bit cache ---------------------------------------------------------------------
+
+def q4_paged_case(A, w, kv_lens, max_len, batch, page_size, num_splits, rotated, seed=0, spare=5):
+    """Paged 4-bit split-K + merge against the oracle's gather-then-dequantise decode, and the
+    paged partials against the contiguous 4-bit kernel's on the same logical cache (bit-identical
+    when both see the same split length)."""
+    announce(f"q4 paged {w.name} B={batch} L={max_len} page={page_size} lens={kv_lens.tolist()[:6]} "
+             f"S={num_splits} rotated={rotated}")
+    q, kq, ks, vq, vs, lens = q4cache.q4_inputs(w, rotated, DEV, salt=seed, kv_lens=kv_lens, max_kv_len=max_len,
+                                                batch=batch)
+    kp, ksp, vp, vsp, table = q4cache.paged(kq, ks, vq, vs, lens, page_size,
+                                            workloads.seed_for(w.name, "q4pages", seed), spare_pages=spare)
+    lens_d, table_d = lens.to(DEV), table.to(DEV)
+    capacity = table.shape[1] * page_size
+    S = A.decode_q4_num_splits(batch, w.hkv, capacity) if num_splits is None else num_splits
+    pm, pl, po = A.decode_splitk_q4_paged(q, kp, ksp, vp, vsp, table_d, lens_d, rotated, S, w.scale)
+    out = A.merge_partials(pm, pl, po, q.dtype)
+    cm, cl, co = A.decode_splitk_q4(q, kq, ks, vq, vs, lens_d, rotated, S, w.scale)
+    torch.cuda.synchronize()
+    if A.decode_chunk_len(capacity, S) == A.decode_chunk_len(max_len, S):
+        assert torch.equal(pm, cm) and torch.equal(pl, cl) and torch.equal(po, co), "paged != contiguous partials"
+    ref = oracle.decode_q4_paged(f64(q), kp.cpu().numpy(), ksp.cpu().double().numpy(), vp.cpu().numpy(),
+                                 vsp.cpu().double().numpy(), table.numpy(), lens.numpy(), w.scale, rotated)
+    assert_close(out, ref, f"q4 paged {w.name} page={page_size} S={S} rotated={rotated}")
+    return out
+
+
+@pytest.mark.parametrize("rotated", [False, True])
+@pytest.mark.parametrize("page_size", [16, 64, 256])
+def test_decode_q4_paged_lengths_and_page_sizes(A, page_size, rotated):
+    """Lengths 0, 1, 15-17 (page edges), 63-65 and the full capacity; garbage codes and NaN
+    scales in spare pages and last-page tails are never used."""
+    lens = torch.tensor([0, 1, 15, 16, 17, 63, 64, 65, 700, 1024], dtype=torch.int32)
+    q4_paged_case(A, DEC, lens, 1024, len(lens), page_size, None, rotated)
+
+
+@pytest.mark.parametrize("S", [1, 3])
+def test_decode_q4_paged_split_longer_than_64_pages(A, S):
+    """Splits of 1024 and 3072 keys over 16-row pages span more than 64 pages, so the kernel
+    reloads its per-lane copy of the block table inside a split."""
+    lens = torch.tensor([3072, 2500, 1025], dtype=torch.int32)
+    q4_paged_case(A, DEC, lens, 3072, 3, 16, S, True)
+
+
+@pytest.mark.parametrize("hq,hkv,d,dtype", [(16, 1, 64, "bf16"), (24, 1, 128, "f16"), (32, 2, 64, "f16")])
+def test_decode_q4_paged_head_layouts(A, hq, hkv, d, dtype):
+    w = workloads.Decode(f"decode_q4p_case_{hq}_{hkv}_{d}_{dtype}", 3, hq, hkv, d, 700, None, 1.0, dtype)
+    q4_paged_case(A, w, torch.tensor([700, 333, 64], dtype=torch.int32), 700, 3, 32, None, True)
+
+
+def test_decode_q4_paged_long_context_full(A, q4_full):
+    """The same 262144-key rotated 4-bit cache in 16-row pages: whole output against the oracle on the
+    dequantised rows, and the paged partials bit-identical to the contiguous kernel's."""
+    announce(f"q4 paged {DEC.name}")
+    f = q4_full
+    q, lens = f["q"], f["lens"]
+    kp, ksp, vp, vsp, table = q4cache.paged(f["kq"], f["ks"], f["vq"], f["vs"], lens, 16,
+                                            workloads.seed_for(DEC.name, "q4pages", 0))
+    lens_d, table_d = lens.to(DEV), table.to(DEV)
+    S = A.decode_q4_num_splits(1, DEC.hkv, DEC.max_kv_len)
+    pm, pl, po = A.decode_splitk_q4_paged(q, kp, ksp, vp, vsp, table_d, lens_d, True, S, DEC.scale)
+    out = A.merge_partials(pm, pl, po, q.dtype)
+    cm, cl, co = A.decode_splitk_q4(q, f["kq"], f["ks"], f["vq"], f["vs"], lens_d, True, S, DEC.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(pm, cm) and torch.equal(pl, cl) and torch.equal(po, co), "paged != contiguous partials"
+    assert_close(out, f["ref"], f"q4 paged {DEC.name}")
 
 
 @pytest.mark.parametrize("d,dtype", [(128, "bf16"), (64, "bf16"), (128, "f16"), (64, "f16")])

@@ -134,6 +134,25 @@ def test_random_q4_decode(A, case):
 
 
 @pytest.mark.parametrize("case", range(8))
+def test_random_q4_paged_decode(A, case):
+    rng = draw(700 + case)
+    hq, hkv, d, dtype, batch, max_len, lens, S = random_decode_shape(rng)
+    rotated = bool(rng.integers(2))
+    page = int(rng.choice([16, 32, 64, 128]))
+    w = workloads.Decode(f"random_q4_paged_{case}", batch, hq, hkv, d, max_len, None, 1.0, dtype)
+    announce(f"{w.name}: B={batch} hq={hq} hkv={hkv} d={d} {dtype} L={max_len} lens={lens.tolist()} S={S} "
+             f"page={page} rotated={rotated}")
+    q, kq, ks, vq, vs, lens = q4cache.q4_inputs(w, rotated, DEV, kv_lens=lens, max_kv_len=max_len, batch=batch)
+    kp, ksp, vp, vsp, table = q4cache.paged(kq, ks, vq, vs, lens, page, workloads.seed_for(w.name, "q4pages", 0),
+                                            spare_pages=int(rng.integers(0, 4)))
+    out = A.decode_q4_paged(q, kp, ksp, vp, vsp, table.to(DEV), lens.to(DEV), rotated, S, w.scale)
+    torch.cuda.synchronize()
+    ref = oracle.decode_q4_paged(f64(q), kp.cpu().numpy(), ksp.cpu().double().numpy(), vp.cpu().numpy(),
+                                 vsp.cpu().double().numpy(), table.numpy(), lens.numpy(), w.scale, rotated)
+    assert_close(out, ref, w.name)
+
+
+@pytest.mark.parametrize("case", range(8))
 def test_random_prefill_long_sampled(A, case):
     """Longer random prefill problems (1000..9000 rows, many tiles and stage wrap-arounds, ragged tails);
     the first, last and random rows of the first and last head against the oracle."""

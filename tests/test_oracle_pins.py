@@ -671,6 +671,62 @@ def test_decode_q4_is_decode_on_dequantised_rows_and_single_key_exact():
         assert np.array_equal(got[1], single) if not rotated else np.max(np.abs(got[1] - single)) <= TOL
 
 
+def q4_pages(codes, scales, lens, ps, seed, spare=0):
+    """Lay a contiguous 4-bit cache (codes [B, H, L, d/2], scales [B, H, L]) out
+    as shuffled pages: each sequence takes ceil(len / ps) pages of a seeded
+    permutation; spare pages and last-page tails hold code 0xFF (-6 at both
+    nibbles) and a NaN scale, which no consumer may read."""
+    B, H, L, half = codes.shape
+    need = [-(-int(n) // ps) for n in lens]
+    total = max(1, sum(need) + spare)
+    perm = np.random.default_rng(seed).permutation(total)
+    pc = np.full((total, H, ps, half), 0xFF, np.uint8)
+    pscale = np.full((total, H, ps), np.nan)
+    table = np.full((B, -(-L // ps)), -1, np.int32)
+    pos = 0
+    for b, n in enumerate(need):
+        for i in range(n):
+            page = perm[pos + i]
+            table[b, i] = page
+            rows = slice(i * ps, min((i + 1) * ps, int(lens[b])))
+            cnt = rows.stop - rows.start
+            pc[page, :, :cnt] = codes[b, :, rows]
+            pscale[page, :, :cnt] = scales[b, :, rows]
+        pos += n
+    return pc, pscale, table
+
+
+@pytest.mark.parametrize("ps", [1, 4, 16])
+def test_decode_q4_paged_is_decode_q4_of_the_gathered_cache(ps):
+    """Pages in a seeded order (garbage in spare pages and tails): bit-identical
+    to the contiguous 4-bit decode, and within TOL of library attention over the
+    dequantised rows of each sequence."""
+    B, hq, hkv, L, d = 3, 4, 2, 40, 16
+    lens = [40, 1, 17]
+    rng = np.random.default_rng(150 + ps)
+    kc = rng.integers(0, 256, (B, hkv, L, d // 2), dtype=np.uint8)
+    vc = rng.integers(0, 256, (B, hkv, L, d // 2), dtype=np.uint8)
+    ks, vs = rng.uniform(0.1, 1, (B, hkv, L)), rng.uniform(0.1, 1, (B, hkv, L))
+    q = gauss(151, B, hq, d)
+    kp, ksp, table = q4_pages(kc, ks, lens, ps, seed=ps, spare=3)
+    vp, vsp, table_v = q4_pages(vc, vs, lens, ps, seed=ps, spare=3)
+    assert np.array_equal(table, table_v)
+    if ps > 1:
+        assert sorted(table[table >= 0].tolist()) != list(range(int((table >= 0).sum())))  # really scattered
+    for rotated in (False, True):
+        got = oracle.decode_q4_paged(q, kp, ksp, vp, vsp, table, lens, 0.25, rotated)
+        assert np.array_equal(got, oracle.decode_q4(q, kc, ks, vc, vs, lens, 0.25, rotated))
+        for b, n in enumerate(lens):
+            K = torch.from_numpy(oracle.dequantize_e2m1_rows(kc[b, :, :n], ks[b, :, :n], rotated))
+            V = torch.from_numpy(oracle.dequantize_e2m1_rows(vc[b, :, :n], vs[b, :, :n], rotated))
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(q[b])[:, None], K.repeat_interleave(hq // hkv, dim=0),
+                V.repeat_interleave(hq // hkv, dim=0), scale=0.25)[:, 0]
+            assert np.max(np.abs(got[b] - ref.numpy())) <= TOL
+    with pytest.raises(ValueError):
+        oracle.decode_q4_paged(q, kp, ksp, vp, vsp, table, [table.shape[1] * ps + 1, 1, 17], 0.25, False)
+
+
 def test_attention_rows_matches_full_output():
     B, hq, n, d = 1, 2, 130, 32
     q, k, v = gauss(62, B, hq, n, d), gauss(63, B, hq, n, d), gauss(64, B, hq, n, d)
