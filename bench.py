@@ -90,7 +90,7 @@ KERNEL_SOURCES = {
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 ONLY = ["all", "step", "prefill_d64", "prefill_d128", "decode", "prefill_causal_gqa", "decode_ragged", "prefill_small",
-        "decode_paged", "append", "decode_q4"]
+        "decode_paged", "append", "decode_q4", "decode_q4_paged"]
 
 # Kernels as rocprofv3 names them (template arguments), per bench label; the
 # labels key the committed traffic counters.
@@ -105,7 +105,8 @@ ROCPROF_NAMES = {
     "merge_partials_kernel<bf16,d128,ragged>": ("merge_partials_kernel<attn::Bf16, 128", "decode_ragged"),
     "decode_splitk_kernel<bf16,d128,paged16>": ("decode_splitk_kernel<attn::Bf16, 128, true>", "decode_paged"),
     "prefill_fwd_kernel<bf16,d128,causal,varlen>": ("prefill_fwd_kernel<attn::Bf16, 128, true, true>", "append"),
-    "decode_q4_kernel<bf16,d128,rotated>": ("decode_q4_kernel<attn::Bf16, 128>", "decode_q4"),
+    "decode_q4_kernel<bf16,d128,rotated>": ("decode_q4_kernel<attn::Bf16, 128, false>", "decode_q4"),
+    "decode_q4_kernel<bf16,d128,rotated,paged16>": ("decode_q4_kernel<attn::Bf16, 128, true>", "decode_q4_paged"),
 }
 
 
@@ -577,6 +578,49 @@ def main() -> int:
              f"{w.name} as rotated 4-bit rows", {"num_splits": S, "bf16_equivalent_bytes": w.kv_bytes(total)}),
             ("merge_partials_kernel<bf16,d128>", "merge_partials_kernel", "hbm",
              w.batch * w.hq * S * (w.d + 2) * 4.0, w.name, {"num_splits": S})], finite(out, "4-bit decode")))
+
+    if want("decode_q4_paged"):
+        w = workloads.WORKLOADS[C4]
+        copies = []
+        for s in (0, 1):
+            q, kc, vc, lens = workloads.decode_inputs(w, device=dev, salt=s)
+            # 16-row pages in a seeded random order; the library's encoder writes each cache row
+            # straight into its pool row (out_rows), as a serving loop appends rows to pages
+            npg = w.max_kv_len // PAGE_SIZE
+            gen = torch.Generator()
+            gen.manual_seed(workloads.seed_for(w.name, "q4pages", s) & ((1 << 63) - 1))
+            table = torch.randperm(w.batch * npg, generator=gen).to(torch.int32).reshape(w.batch, npg).to(dev)
+            pos = torch.arange(w.max_kv_len, device=dev)
+            kh = torch.arange(w.hkv, device=dev)[:, None]
+            dest = ((table[:, pos // PAGE_SIZE].long()[:, None, :] * w.hkv + kh) * PAGE_SIZE
+                    + pos % PAGE_SIZE).to(torch.int32).reshape(-1)
+            pools = []
+            for cache in (kc, vc):
+                pc = torch.empty((w.batch * npg, w.hkv, PAGE_SIZE, w.d // 2), dtype=torch.uint8, device=dev)
+                psc = torch.empty((w.batch * npg, w.hkv, PAGE_SIZE), dtype=torch.float32, device=dev)
+                A.kv_quantize_q4(cache.reshape(-1, w.d), True, dest, pc.view(-1, w.d // 2), psc.view(-1))
+                pools += [pc, psc]
+            del kc, vc, dest
+            copies.append((q, *pools, table, lens.to(dev)))
+        S = A.decode_q4_num_splits(w.batch, w.hkv, w.max_kv_len)
+        part = partials(w, S)
+        out = torch.empty((w.batch, w.hq, w.d), dtype=torch.bfloat16, device=dev)
+        total = int(copies[0][6].sum())
+        q4_bytes = 2.0 * w.hkv * total * (w.d // 2 + 4)
+
+        def launch(i, ev, w=w, copies=copies, S=S, part=part, out=out):
+            q, kp, ksp, vp, vsp, table, lens = copies[i % 2]
+            mark(ev, 0)
+            A.decode_splitk_q4_paged(q, kp, ksp, vp, vsp, table, lens, True, S, w.scale, partials=part)
+            mark(ev, 1)
+            A.merge_partials(*part, torch.bfloat16, out=out)
+            mark(ev, 2)
+        other_regions.append(Region("decode_q4_paged", launch, [
+            (f"decode_q4_kernel<bf16,d128,rotated,paged{PAGE_SIZE}>", "decode_q4_kernel", "hbm", q4_bytes,
+             f"{w.name} as rotated 4-bit rows in {PAGE_SIZE}-row pages",
+             {"num_splits": S, "bf16_equivalent_bytes": w.kv_bytes(total)}),
+            ("merge_partials_kernel<bf16,d128>", "merge_partials_kernel", "hbm",
+             w.batch * w.hq * S * (w.d + 2) * 4.0, w.name, {"num_splits": S})], finite(out, "paged 4-bit decode")))
     torch.cuda.synchronize()
 
     regions = step_regions + other_regions
@@ -659,6 +703,8 @@ def main() -> int:
                         "attn_prefill_varlen_fwd, wall clock, outside the step"),
         "decode_q4": extra("decode_q4", lambda r: r.kernels[0][3], "GB/s",
                            "attn_decode_splitk_q4 + attn_merge_partials, wall clock, outside the step"),
+        "decode_q4_paged": extra("decode_q4_paged", lambda r: r.kernels[0][3], "GB/s",
+                                 "attn_decode_splitk_q4_paged + attn_merge_partials, wall clock, outside the step"),
         "roofline": roofline,
         "kernels": kernels,
     }

@@ -19,7 +19,8 @@ Entry points (same names as the C ABI):
   scale)`` -- ``attn_decode_splitk_q4_paged``
 * ``kv_quantize_q4(x, rotated, out_rows, codes, scales)`` -- ``attn_kv_quantize_q4``
 * ``merge_partials(part_m, part_l, part_o, out_dtype)`` -- ``attn_merge_partials``
-* ``decode(...)``, ``decode_paged(...)``, ``decode_q4(...)``, ``decode_q4_paged(...)`` -- split-K then merge, back to back on one stream
+* ``decode(...)``, ``decode_paged(...)``, ``decode_q4(...)``, ``decode_q4_paged(...)`` -- split-K then merge, back to
+  back on one stream
 * ``decode_noalloc(q, k_cache, v_cache, kv_lens, num_splits, scale)`` -- ``attn_decode_noalloc``: the same
   split-K and merge with the partial states in the library's fixed scratch array (no workspace)
 * ``decode_num_splits``, ``decode_q4_num_splits``, ``decode_chunk_len``, ``decode_workspace_bytes`` -- host helpers
@@ -36,8 +37,8 @@ from . import _lib
 from ._lib import ATTN_BF16, ATTN_F16, AttnError  # noqa: F401
 
 __all__ = ["prefill_fwd", "prefill_varlen_fwd", "decode_splitk", "decode_splitk_paged", "decode_splitk_q4", "decode_q4",
-           "decode_splitk_q4_paged", "decode_q4_paged", "kv_quantize_q4", "merge_partials", "decode", "decode_paged", "decode_noalloc",
-           "decode_num_splits", "decode_q4_num_splits", "decode_chunk_len", "decode_workspace_bytes", "AttnError"]
+           "decode_splitk_q4_paged", "decode_q4_paged", "kv_quantize_q4", "merge_partials", "decode", "decode_paged",
+           "decode_noalloc", "decode_num_splits", "decode_q4_num_splits", "decode_chunk_len", "decode_workspace_bytes", "AttnError"]
 
 _DTYPES = {torch.bfloat16: ATTN_BF16, torch.float16: ATTN_F16}
 
