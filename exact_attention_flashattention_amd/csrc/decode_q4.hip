@@ -154,8 +154,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const int qgrp = blockIdx.y / hkv;
   const int b = blockIdx.z;
   // split index rotated by the head's number, as in decode_splitk.hip (spreads the
-  // waves that run together over different offsets of their heads' cache regions)
-  const int split = (int)((blockIdx.x + (unsigned)(b * hkv + kh) * 5u) % (unsigned)num_splits);
+  // waves that run together over different offsets of their heads' cache regions).
+  // Paged: not rotated, so the KV heads of one split -- whose rows share each page,
+  // and whose scales share 128-byte lines when pages are 16 rows -- land on one XCD
+  // (workgroups go round-robin to the 8 XCDs; the split count is then a multiple of 8).
+  const int split = PAGED ? (int)blockIdx.x
+                          : (int)((blockIdx.x + (unsigned)(b * hkv + kh) * 5u) % (unsigned)num_splits);
   const int qi = qgrp * 16 + r;
   const bool qvalid = qi < g;
   const int h = kh * g + (qvalid ? qi : 0);
